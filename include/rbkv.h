@@ -1,0 +1,201 @@
+/*
+ * rbkv.h -- C ABI of librbkv: ragged-batch attention over a blocked (paged) KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations make up one forward pass of attention over a ragged batch:
+ *
+ *   ragged_batch_finalize     once per forward pass: validate the batch on the host and
+ *                             build its device metadata (token offsets / cu_seqlens,
+ *                             seen tokens, block tables, per-token sequence and
+ *                             position, and the list of work items).
+ *   blocked_kv_append_rotary  once per layer: rotate the new Q and K rows at their
+ *                             absolute positions and store rotated K and raw V into the
+ *                             sequence's KV blocks.
+ *   ragged_blocked_attention  once per layer: causal softmax(Q K^T / sqrt(d)) V per
+ *                             sequence over its blocks, with grouped-query heads.
+ *
+ * The ragged layout follows "DeepSpeed Inference v2 source tour" (pyshine.com), section
+ * "Ragged batches: packing a whole server into four tensors": the live tokens of all
+ * sequences sit edge to edge in one stream with no padding, a metadata buffer records
+ * where each sequence's tokens start and stop, a tokens-to-sequence map rides beside
+ * it, and kernels read per-sequence integer block ids to address the KV pool
+ * directly.  The blocked pool (flat, block-indexed, with key and value views) follows
+ * section "The front desk: put, query, can_schedule" of the same page.  Prefill chunks
+ * and single-token decodes share one batch (Dynamic SplitFuse, "DeepSpeed-Inference
+ * and DeepSpeed-MII" tutorial, sections 10.3 and 10.10).
+ *
+ * Conventions
+ * -----------
+ * - Every call returns an rbkv_status and never throws or aborts.  All argument checks
+ *   run on the host before anything is launched or written; on error nothing is
+ *   launched.  (Non-throwing verdicts follow can_schedule's SchedulingResult, same
+ *   page, "The front desk" section; catching a buffer in the wrong place at call time
+ *   rather than as a kernel fault follows InferenceParameter, section "Policies,
+ *   containers, and a metaclass that checks your weights".)
+ * - The caller owns all memory.  The library allocates no device memory, keeps no
+ *   mutable global state and never synchronises the stream; every call only enqueues
+ *   work on the given stream.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Device
+ *   buffers must belong to the current HIP device.
+ * - Element types: RBKV_DTYPE_F32 (float) or RBKV_DTYPE_BF16 (bfloat16 bit patterns).
+ *   Integers are int32.  All multi-dimensional arrays are dense, row-major.
+ *
+ * Layouts (d = head_dim, Hq = n_q_heads, Hkv = n_kv_heads, G = Hq / Hkv, bs = block_size)
+ *   qkv      [T][Hq + 2*Hkv][d]   fused new rows: Q heads, then K heads, then V heads
+ *   kv_pool  [num_blocks][2][Hkv][bs][d]   index 0 = keys, 1 = values; key p of a
+ *            sequence lives in block block_ids[p / bs] at slot p % bs
+ *   out      [T][Hq][d]           attention output, same dtype as qkv
+ * Query head h reads kv head h / G.  Token k of a sequence with `seen` cached tokens
+ * sits at position seen + k and attends to keys 0 .. seen + k of its own sequence.
+ */
+#ifndef RBKV_H
+#define RBKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rbkv_status;
+enum {
+  RBKV_OK = 0,
+  RBKV_ERR_INVALID_ARG = 1, /* null pointer, negative count, n_new < 1, shape mismatch */
+  RBKV_ERR_CAPACITY = 2,    /* T > max_tokens or S > max_seqs */
+  RBKV_ERR_BLOCKS = 3,      /* block list too short, id out of range, id used twice */
+  RBKV_ERR_UNSUPPORTED = 4, /* head_dim, block_size, dtype, group size or limits */
+  RBKV_ERR_WORKSPACE = 5,   /* a caller buffer is smaller than the size query says */
+  RBKV_ERR_DEVICE_PTR = 6,  /* buffer is not device (or pinned host) memory of the
+                               current device, or its allocation is too small */
+  RBKV_ERR_HIP = 7          /* a HIP call or kernel launch failed */
+};
+
+enum { RBKV_DTYPE_F32 = 0, RBKV_DTYPE_BF16 = 1 };
+
+/* Static shape of one attention layer and its KV pool, plus the batch capacities.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32, 64, 128};
+ * n_q_heads = G * n_kv_heads with 1 <= G <= 16; 1 <= max_seqs <= 2048;
+ * 1 <= max_tokens <= 1048576; 1 <= num_blocks <= 2^26.
+ * The engine limits quoted on the pages are max_tokens = 8192 and max_seqs = 256
+ * ("DeepSpeed-Inference and DeepSpeed-MII", section 10.3). */
+typedef struct rbkv_shape {
+  int32_t max_tokens;
+  int32_t max_seqs;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+} rbkv_shape;
+
+/* A finalized batch: host-side counts plus device pointers into the caller's metadata
+ * buffer.  Filled by ragged_batch_finalize; read-only for the caller; valid as long as
+ * that buffer is (one batch serves every layer of the forward pass).  The device
+ * arrays are int32:
+ *   cu_seqlens[S+1]     start of each sequence's tokens in the packed stream
+ *   seen[S]             tokens already cached before this pass
+ *   kv_len[S]           seen + new tokens
+ *   block_offsets[S+1]  start of each sequence's block table in block_ids
+ *   block_ids[n_blocks_used]  the first ceil(kv_len / block_size) ids of each list
+ *   token_to_seq[T]     owning sequence of each packed token
+ *   pos[T]              absolute position of each packed token
+ *   decode_work, prefill_work, combine_work: work-item records (4 int32 each) of the
+ *                       three attention kernels; their format is internal. */
+typedef struct rbkv_batch {
+  rbkv_shape shape; /* the shape this batch was built for */
+  int32_t S;
+  int32_t T;
+  int32_t n_blocks_used;
+  int32_t split_tiles;   /* keys per decode split, in units of 64 keys */
+  int32_t n_decode_items;
+  int32_t n_prefill_items;
+  int32_t n_partials;    /* split-K partial-result slots needed in the workspace */
+  int32_t n_combine_items;
+  const int32_t* cu_seqlens;
+  const int32_t* seen;
+  const int32_t* kv_len;
+  const int32_t* block_offsets;
+  const int32_t* block_ids;
+  const int32_t* token_to_seq;
+  const int32_t* pos;
+  const int32_t* decode_work;
+  const int32_t* prefill_work;
+  const int32_t* combine_work;
+} rbkv_batch;
+
+/* Static string naming a status code (never NULL). */
+const char* rbkv_status_string(rbkv_status status);
+
+/* Sizes of the two caller-owned buffers ragged_batch_finalize needs for `shape`:
+ * device metadata (dev_bytes) and page-locked host staging (host_pinned_bytes, from
+ * hipHostMalloc).  They are the "preallocated host buffers" and device tensors of the
+ * ragged batch ("DeepSpeed Inference v2 source tour", section "Ragged batches").
+ * Either output pointer may be NULL.  Pure host computation. */
+rbkv_status rbkv_metadata_bytes(const rbkv_shape* shape, size_t* dev_bytes,
+                                size_t* host_pinned_bytes);
+
+/* Device workspace ragged_blocked_attention needs for `batch` (split-K partial
+ * results, the "out scratch" handed to the blocked attention kernel in the same
+ * section).  0 when no decode is split.  Pure host computation. */
+rbkv_status rbkv_workspace_bytes(const rbkv_shape* shape, const rbkv_batch* batch,
+                                 size_t* bytes);
+
+/* Build the device metadata of one ragged batch (the pages' insert_sequence then
+ * finalize, "DeepSpeed Inference v2 source tour", section "Ragged batches").
+ *
+ *   S                  number of sequences, 0 <= S <= max_seqs (S = 0: no-op, OK)
+ *   n_new[S]           new tokens per sequence (>= 1), host memory
+ *   seen[S]            tokens already in the cache per sequence (>= 0), host memory
+ *   block_ids[S]       host array of S host pointers: sequence i's block-id list
+ *   n_block_ids[S]     length of each list; must be >= ceil((seen+n_new)/block_size);
+ *                      only that many leading ids are used.  Used ids must lie in
+ *                      [0, num_blocks) and be distinct across the whole batch.
+ *   host_pinned        page-locked staging buffer (hipHostMalloc) of at least the
+ *                      size rbkv_metadata_bytes gives; it must stay untouched until
+ *                      the stream has passed this call (the upload is asynchronous).
+ *   dev_meta           device buffer of at least the size rbkv_metadata_bytes gives.
+ *   out                filled on success (host struct).
+ * Errors: INVALID_ARG, CAPACITY (S > max_seqs, sum(n_new) > max_tokens), BLOCKS,
+ * UNSUPPORTED, WORKSPACE (a buffer smaller than required), DEVICE_PTR, HIP.
+ * Enqueues one host-to-device copy and one kernel on `stream`. */
+rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int32_t* n_new,
+                                  const int32_t* seen, const int32_t* const* block_ids,
+                                  const int32_t* n_block_ids, void* host_pinned,
+                                  size_t host_pinned_bytes, void* dev_meta,
+                                  size_t dev_meta_bytes, void* stream, rbkv_batch* out);
+
+/* Rotary position embedding and KV append for one layer.
+ *   qkv       device [T][Hq + 2*Hkv][d]; the Q heads are rotated IN PLACE, K and V rows
+ *             are left as they are.
+ *   kv_pool   device [num_blocks][2][Hkv][bs][d]; for each new token at position p the
+ *             rotated K and the raw V are written to block block_ids[p / bs], slot
+ *             p % bs, of its sequence.  No other pool element is touched.
+ *   rope_base > 0: rotate each pair (x_j, x_{j + d/2}) by the angle p * base^(-2j/d)
+ *             (angle, sine and cosine in float64, the rotation in float64, one
+ *             round-to-nearest-even into the storage dtype); <= 0: no rotation.
+ * Errors: INVALID_ARG (null, batch built for another shape), DEVICE_PTR, HIP. */
+rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* batch,
+                                     void* qkv, void* kv_pool, double rope_base,
+                                     void* stream);
+
+/* Causal grouped-query attention of every new token over its sequence's blocks:
+ * out[t][h] = sum_p softmax_p(q_t,h . K[p, h/G] / sqrt(d)) V[p, h/G], p = 0 .. pos[t].
+ *   qkv       device [T][Hq + 2*Hkv][d] (read: the rotated Q heads)
+ *   kv_pool   device pool already holding this pass's keys and values
+ *   out       device [T][Hq][d], written entirely
+ *   workspace device scratch of at least rbkv_workspace_bytes (may be NULL if 0)
+ * Single-token decodes run as split-K streaming over 64-key tiles followed by a
+ * log-sum-exp combine; bf16 prefill chunks run on MFMA tiles; float32 runs on the
+ * vector ALUs throughout.  Accumulation is float32.
+ * Errors: INVALID_ARG, WORKSPACE, DEVICE_PTR, HIP. */
+rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
+                                     const void* qkv, const void* kv_pool, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBKV_H */

@@ -1,0 +1,186 @@
+"""Python binding of librbkv: ragged-batch attention over a blocked KV cache on MI355X.
+
+Argument marshalling only.  Every step of the path -- metadata build, rotary append,
+attention -- runs in the library's gfx950 kernels behind its C ABI (``include/rbkv.h``);
+this module converts shapes, host arrays and device pointers and returns the C status
+codes.  PyTorch is used only to own device memory and streams.  Importing this module
+does not need a GPU, but it needs the built library: it raises if ``librbkv.so`` is
+missing (build it with ``python -m ragged_blocked_kv_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "RbkvError", "Shape", "Batch", "lib", "status_string", "check",
+    "rbkv_metadata_bytes", "rbkv_workspace_bytes", "ragged_batch_finalize",
+    "blocked_kv_append_rotary", "ragged_blocked_attention", "EXPORTED_SYMBOLS",
+    "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
+    "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "DTYPE_F32", "DTYPE_BF16",
+]
+
+OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_BLOCKS, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+ERR_WORKSPACE, ERR_DEVICE_PTR, ERR_HIP = 5, 6, 7
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librbkv.so")
+
+EXPORTED_SYMBOLS = (
+    "rbkv_status_string",
+    "rbkv_metadata_bytes",
+    "rbkv_workspace_bytes",
+    "ragged_batch_finalize",
+    "blocked_kv_append_rotary",
+    "ragged_blocked_attention",
+)
+
+
+class RbkvError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = int(status)
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "max_tokens", "max_seqs", "num_blocks", "block_size", "n_q_heads", "n_kv_heads",
+        "head_dim", "dtype")]
+
+    @classmethod
+    def make(cls, *, max_tokens, max_seqs, num_blocks, block_size, n_q_heads, n_kv_heads,
+             head_dim, dtype):
+        dt = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}.get(dtype, dtype)
+        return cls(int(max_tokens), int(max_seqs), int(num_blocks), int(block_size),
+                   int(n_q_heads), int(n_kv_heads), int(head_dim), int(dt))
+
+
+_P = ctypes.POINTER(ctypes.c_int32)
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("shape", Shape)] + [(n, ctypes.c_int32) for n in (
+        "S", "T", "n_blocks_used", "split_tiles", "n_decode_items", "n_prefill_items",
+        "n_partials", "n_combine_items")] + [(n, ctypes.c_void_p) for n in (
+        "cu_seqlens", "seen", "kv_len", "block_offsets", "block_ids", "token_to_seq", "pos",
+        "decode_work", "prefill_work", "combine_work")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librbkv (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"librbkv.so not built at {LIB_PATH}; run "
+                              "`python -m ragged_blocked_kv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.rbkv_status_string.restype = ctypes.c_char_p
+        L.rbkv_status_string.argtypes = [ctypes.c_int32]
+        L.rbkv_metadata_bytes.restype = ctypes.c_int32
+        L.rbkv_metadata_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.rbkv_workspace_bytes.restype = ctypes.c_int32
+        L.rbkv_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Batch),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+        L.ragged_batch_finalize.restype = ctypes.c_int32
+        L.ragged_batch_finalize.argtypes = [
+            ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, ctypes.POINTER(_P), _P,
+            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.c_void_p, ctypes.POINTER(Batch)]
+        L.blocked_kv_append_rotary.restype = ctypes.c_int32
+        L.blocked_kv_append_rotary.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_double, ctypes.c_void_p]
+        L.ragged_blocked_attention.restype = ctypes.c_int32
+        L.ragged_blocked_attention.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rbkv_status_string(int(status)).decode()
+
+
+def check(status: int, what: str = "rbkv") -> None:
+    if status != OK:
+        raise RbkvError(status, what)
+
+
+def _ptr(x) -> Optional[int]:
+    """Raw address of a tensor / integer / None."""
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return int(stream.cuda_stream)
+    return int(stream)
+
+
+def rbkv_metadata_bytes(shape: Shape):
+    """(status, dev_bytes, host_pinned_bytes)."""
+    d, h = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib().rbkv_metadata_bytes(ctypes.byref(shape), ctypes.byref(d), ctypes.byref(h))
+    return st, d.value, h.value
+
+
+def rbkv_workspace_bytes(shape: Shape, batch: Batch):
+    """(status, bytes)."""
+    b = ctypes.c_size_t(0)
+    st = lib().rbkv_workspace_bytes(ctypes.byref(shape), ctypes.byref(batch), ctypes.byref(b))
+    return st, b.value
+
+
+class _HostLists:
+    """Keeps the int32 host arrays alive for the duration of a finalize call."""
+
+    def __init__(self, n_new, seen, block_lists):
+        self.n_new = np.ascontiguousarray(np.asarray(n_new, dtype=np.int32))
+        self.seen = np.ascontiguousarray(np.asarray(seen, dtype=np.int32))
+        self.lists = [np.ascontiguousarray(np.asarray(b, dtype=np.int32)) for b in block_lists]
+        S = len(self.lists)
+        self.ptrs = (_P * max(S, 1))(*[l.ctypes.data_as(_P) for l in self.lists])
+        self.lens = np.ascontiguousarray(np.array([len(l) for l in self.lists], dtype=np.int32))
+
+
+def ragged_batch_finalize(shape: Shape, n_new: Sequence[int], seen: Sequence[int],
+                          block_lists: Sequence[Sequence[int]], host_pinned, host_pinned_bytes,
+                          dev_meta, dev_meta_bytes, stream=None, *, S: Optional[int] = None,
+                          null_lists: bool = False):
+    """(status, Batch).  ``host_pinned``/``dev_meta`` are tensors or raw addresses."""
+    h = _HostLists(n_new, seen, block_lists)
+    S = len(h.lists) if S is None else S
+    out = Batch()
+    st = lib().ragged_batch_finalize(
+        ctypes.byref(shape), int(S), h.n_new.ctypes.data_as(_P), h.seen.ctypes.data_as(_P),
+        None if null_lists else h.ptrs, h.lens.ctypes.data_as(_P), _ptr(host_pinned),
+        int(host_pinned_bytes), _ptr(dev_meta), int(dev_meta_bytes), _stream(stream),
+        ctypes.byref(out))
+    return st, out
+
+
+def blocked_kv_append_rotary(shape: Shape, batch: Batch, qkv, kv_pool, rope_base: float,
+                             stream=None) -> int:
+    return lib().blocked_kv_append_rotary(ctypes.byref(shape), ctypes.byref(batch), _ptr(qkv),
+                                          _ptr(kv_pool), float(rope_base), _stream(stream))
+
+
+def ragged_blocked_attention(shape: Shape, batch: Batch, qkv, kv_pool, out, workspace,
+                             workspace_bytes: int, stream=None) -> int:
+    return lib().ragged_blocked_attention(ctypes.byref(shape), ctypes.byref(batch), _ptr(qkv),
+                                          _ptr(kv_pool), _ptr(out), _ptr(workspace),
+                                          int(workspace_bytes), _stream(stream))

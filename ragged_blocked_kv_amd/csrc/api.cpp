@@ -1,0 +1,324 @@
+// Host side of librbkv: argument validation, batch planning, staging and launches.
+// Every check runs before any HIP call, so each error path is testable without a GPU.
+#include <string.h>
+
+#include <vector>
+
+#include "rbkv_internal.h"
+
+using namespace rbkv;
+
+namespace {
+
+bool shape_supported(const rbkv_shape& s, rbkv_status* st) {
+  if (s.max_tokens < 1 || s.max_seqs < 1 || s.num_blocks < 1 || s.n_q_heads < 1 ||
+      s.n_kv_heads < 1 || s.block_size < 1 || s.head_dim < 1) {
+    *st = RBKV_ERR_INVALID_ARG;
+    return false;
+  }
+  const bool ok_d = s.head_dim == 64 || s.head_dim == 128;
+  const bool ok_bs = s.block_size == 16 || s.block_size == 32 || s.block_size == 64 ||
+                     s.block_size == 128;
+  const bool ok_dt = s.dtype == RBKV_DTYPE_F32 || s.dtype == RBKV_DTYPE_BF16;
+  const bool ok_g = s.n_q_heads % s.n_kv_heads == 0 &&
+                    s.n_q_heads / s.n_kv_heads <= MAX_GROUP;
+  const bool ok_lim = s.max_seqs <= MAX_SEQS_LIMIT && s.max_tokens <= MAX_TOKENS_LIMIT &&
+                      s.num_blocks <= MAX_BLOCKS_LIMIT && s.n_q_heads <= 1024;
+  if (!(ok_d && ok_bs && ok_dt && ok_g && ok_lim)) {
+    *st = RBKV_ERR_UNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+rbkv_status check_shape(const rbkv_shape* s) {
+  if (!s) return RBKV_ERR_INVALID_ARG;
+  rbkv_status st = RBKV_OK;
+  return shape_supported(*s, &st) ? RBKV_OK : st;
+}
+
+size_t elem_bytes(const rbkv_shape& s) { return s.dtype == RBKV_DTYPE_F32 ? 4 : 2; }
+
+// A device buffer must be device (or managed) memory of the current device, and its
+// allocation must extend at least `bytes` past `p`.
+rbkv_status check_device(const void* p, size_t bytes) {
+  if (!p) return RBKV_ERR_INVALID_ARG;
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_DEVICE_PTR;
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+    return RBKV_ERR_DEVICE_PTR;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return RBKV_ERR_HIP;
+  if (a.device != dev) return RBKV_ERR_DEVICE_PTR;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_DEVICE_PTR;
+  }
+  if ((const char*)p + bytes > (const char*)base + size) return RBKV_ERR_DEVICE_PTR;
+  return RBKV_OK;
+}
+
+rbkv_status check_pinned(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_DEVICE_PTR;
+  }
+  return a.type == hipMemoryTypeHost ? RBKV_OK : RBKV_ERR_DEVICE_PTR;
+}
+
+bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
+  return memcmp(&a, &b, sizeof(rbkv_shape)) == 0;
+}
+
+// Split size for single-token decodes: about DECODE_TARGET_ITEMS items overall.
+int32_t choose_split_tiles(int64_t decode_tiles_total) {
+  int64_t st = cdiv64(decode_tiles_total, DECODE_TARGET_ITEMS);
+  if (st < MIN_SPLIT_TILES) st = MIN_SPLIT_TILES;
+  if (st > MAX_SPLIT_TILES) st = MAX_SPLIT_TILES;
+  return (int32_t)st;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rbkv_status_string(rbkv_status status) {
+  switch (status) {
+    case RBKV_OK: return "ok";
+    case RBKV_ERR_INVALID_ARG: return "invalid argument";
+    case RBKV_ERR_CAPACITY: return "batch exceeds max_tokens or max_seqs";
+    case RBKV_ERR_BLOCKS: return "block list too short, id out of range or id used twice";
+    case RBKV_ERR_UNSUPPORTED: return "unsupported shape (head_dim, block_size, dtype, group)";
+    case RBKV_ERR_WORKSPACE: return "buffer smaller than the size query requires";
+    case RBKV_ERR_DEVICE_PTR: return "buffer is not memory of the expected kind on this device";
+    case RBKV_ERR_HIP: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+rbkv_status rbkv_metadata_bytes(const rbkv_shape* shape, size_t* dev_bytes,
+                                size_t* host_pinned_bytes) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  MetaLayout L = meta_layout(*shape);
+  if (dev_bytes) *dev_bytes = L.total;
+  if (host_pinned_bytes) *host_pinned_bytes = L.staging_bytes;
+  return RBKV_OK;
+}
+
+rbkv_status rbkv_workspace_bytes(const rbkv_shape* shape, const rbkv_batch* batch,
+                                 size_t* bytes) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (!batch || !bytes) return RBKV_ERR_INVALID_ARG;
+  if (!same_shape(batch->shape, *shape)) return RBKV_ERR_INVALID_ARG;
+  const int32_t G = shape->n_q_heads / shape->n_kv_heads;
+  *bytes = (size_t)batch->n_partials * partial_floats(G, shape->head_dim) * sizeof(float);
+  return RBKV_OK;
+}
+
+rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int32_t* n_new,
+                                  const int32_t* seen, const int32_t* const* block_ids,
+                                  const int32_t* n_block_ids, void* host_pinned,
+                                  size_t host_pinned_bytes, void* dev_meta,
+                                  size_t dev_meta_bytes, void* stream, rbkv_batch* out) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  const rbkv_shape& s = *shape;
+  if (!out || S < 0) return RBKV_ERR_INVALID_ARG;
+  if (S > s.max_seqs) return RBKV_ERR_CAPACITY;
+  if (S > 0 && (!n_new || !seen || !block_ids || !n_block_ids)) return RBKV_ERR_INVALID_ARG;
+  if (!host_pinned || !dev_meta) return RBKV_ERR_INVALID_ARG;
+  const MetaLayout L = meta_layout(s);
+  if (host_pinned_bytes < L.staging_bytes || dev_meta_bytes < L.total)
+    return RBKV_ERR_WORKSPACE;
+
+  const int32_t Hkv = s.n_kv_heads;
+  const int32_t G = s.n_q_heads / Hkv;
+  const bool mfma = s.dtype == RBKV_DTYPE_BF16;
+  const int32_t qtt = q_tile_tokens(G);
+
+  // Per-sequence checks, totals and the decode tile count.
+  int64_t T = 0, nblk = 0, dec_tiles = 0;
+  for (int32_t i = 0; i < S; ++i) {
+    if (n_new[i] < 1 || seen[i] < 0) return RBKV_ERR_INVALID_ARG;
+    T += n_new[i];
+    if (T > s.max_tokens) return RBKV_ERR_CAPACITY;
+    const int64_t L_i = (int64_t)seen[i] + n_new[i];
+    const int64_t B_i = cdiv64(L_i, s.block_size);
+    if (B_i > s.num_blocks) return RBKV_ERR_BLOCKS;
+    if (!block_ids[i] || n_block_ids[i] < B_i) return RBKV_ERR_BLOCKS;
+    nblk += B_i;
+    if (nblk > s.num_blocks) return RBKV_ERR_BLOCKS;  // ids are distinct, so they cannot fit
+    if (n_new[i] == 1) dec_tiles += (int64_t)Hkv * cdiv64(L_i, KT);
+  }
+  // Block ids: in range and distinct across the batch.
+  if (S > 0) {
+    std::vector<uint8_t> used((size_t)s.num_blocks, 0);
+    for (int32_t i = 0; i < S; ++i) {
+      const int64_t B_i = cdiv64((int64_t)seen[i] + n_new[i], s.block_size);
+      for (int64_t k = 0; k < B_i; ++k) {
+        const int32_t id = block_ids[i][k];
+        if (id < 0 || id >= s.num_blocks) return RBKV_ERR_BLOCKS;
+        if (used[(size_t)id]) return RBKV_ERR_BLOCKS;
+        used[(size_t)id] = 1;
+      }
+    }
+  }
+
+  const int32_t split = choose_split_tiles(dec_tiles);
+  int64_t ndec = 0, npre = 0, npart = 0, ncomb = 0;
+  for (int32_t i = 0; i < S; ++i) {
+    SeqPlan p = plan_sequence(n_new[i], seen[i], Hkv, split, mfma, qtt);
+    ndec += p.dec_items;
+    npre += p.pre_items;
+    npart += p.partials;
+    ncomb += p.comb_items;
+  }
+  const Caps caps = work_caps(s);  // bounds every valid batch; checked to fail loudly
+  if (ndec > caps.dec || npre > caps.pre || ncomb > caps.comb || npart > caps.dec ||
+      ndec > INT32_MAX)
+    return RBKV_ERR_CAPACITY;
+
+  char* dm = (char*)dev_meta;
+  rbkv_batch b;
+  memset(&b, 0, sizeof(b));
+  b.shape = s;
+  b.S = S;
+  b.T = (int32_t)T;
+  b.n_blocks_used = (int32_t)nblk;
+  b.split_tiles = split;
+  b.n_decode_items = (int32_t)ndec;
+  b.n_prefill_items = (int32_t)npre;
+  b.n_partials = (int32_t)npart;
+  b.n_combine_items = (int32_t)ncomb;
+  b.cu_seqlens = (const int32_t*)(dm + L.cu);
+  b.seen = (const int32_t*)(dm + L.seen);
+  b.kv_len = (const int32_t*)(dm + L.kv_len);
+  b.block_offsets = (const int32_t*)(dm + L.block_off);
+  b.block_ids = (const int32_t*)(dm + L.block_ids);
+  b.token_to_seq = (const int32_t*)(dm + L.tok2seq);
+  b.pos = (const int32_t*)(dm + L.pos);
+  b.decode_work = (const int32_t*)(dm + L.dec);
+  b.prefill_work = (const int32_t*)(dm + L.pre);
+  b.combine_work = (const int32_t*)(dm + L.comb);
+  if (S == 0) {  // nothing to build or launch
+    *out = b;
+    return RBKV_OK;
+  }
+
+  // Pointer kinds (the first HIP calls).
+  if ((st = check_pinned(host_pinned)) != RBKV_OK) return st;
+  if ((st = check_device(dev_meta, L.total)) != RBKV_OK) return st;
+
+  // Pack header, n_new, seen and the flat block tables into the staging area.
+  int32_t* hp = (int32_t*)host_pinned;
+  memset(hp, 0, HDR_INTS * 4);
+  hp[H_S] = S;
+  hp[H_T] = (int32_t)T;
+  hp[H_NBLK] = (int32_t)nblk;
+  hp[H_SPLIT] = split;
+  hp[H_HKV] = Hkv;
+  hp[H_MFMA] = mfma ? 1 : 0;
+  hp[H_QTT] = qtt;
+  hp[H_NDEC] = (int32_t)ndec;
+  hp[H_NPRE] = (int32_t)npre;
+  hp[H_NPART] = (int32_t)npart;
+  hp[H_NCOMB] = (int32_t)ncomb;
+  int32_t* hn = (int32_t*)((char*)host_pinned + L.n_new);
+  int32_t* hs = (int32_t*)((char*)host_pinned + L.seen);
+  int32_t* hb = (int32_t*)((char*)host_pinned + L.block_ids);
+  memcpy(hn, n_new, (size_t)S * 4);
+  memcpy(hs, seen, (size_t)S * 4);
+  int64_t at = 0;
+  for (int32_t i = 0; i < S; ++i) {
+    const int64_t B_i = cdiv64((int64_t)seen[i] + n_new[i], s.block_size);
+    memcpy(hb + at, block_ids[i], (size_t)B_i * 4);
+    at += B_i;
+  }
+
+  hipStream_t hs_stream = (hipStream_t)stream;
+  // One copy covers header, n_new, seen (capacity-sized) and the used block ids.
+  const size_t copy_bytes = L.block_ids + (size_t)nblk * 4;
+  if (hipMemcpyAsync(dm, host_pinned, copy_bytes, hipMemcpyHostToDevice, hs_stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  if (launch_meta_build((const int32_t*)dm, (int32_t*)(dm + L.cu), (int32_t*)(dm + L.kv_len),
+                        (int32_t*)(dm + L.block_off), (int32_t*)(dm + L.tok2seq),
+                        (int32_t*)(dm + L.pos), (int32_t*)(dm + L.dec),
+                        (int32_t*)(dm + L.pre), (int32_t*)(dm + L.comb), s.block_size,
+                        s.max_seqs, hs_stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  *out = b;
+  return RBKV_OK;
+}
+
+rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* batch,
+                                     void* qkv, void* kv_pool, double rope_base,
+                                     void* stream) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (!batch || !qkv || !kv_pool) return RBKV_ERR_INVALID_ARG;
+  const rbkv_shape& s = *shape;
+  if (!same_shape(batch->shape, s)) return RBKV_ERR_INVALID_ARG;
+  if (batch->T < 0 || batch->T > s.max_tokens) return RBKV_ERR_INVALID_ARG;
+  if (batch->T == 0) return RBKV_OK;
+  const size_t e = elem_bytes(s);
+  const size_t qkv_bytes = (size_t)batch->T * (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * e;
+  const size_t pool_bytes = (size_t)s.num_blocks * 2 * s.n_kv_heads * s.block_size * s.head_dim * e;
+  if ((st = check_device(qkv, qkv_bytes)) != RBKV_OK) return st;
+  if ((st = check_device(kv_pool, pool_bytes)) != RBKV_OK) return st;
+  if (launch_append_rotary(s, *batch, qkv, kv_pool, rope_base, (hipStream_t)stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
+rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
+                                     const void* qkv, const void* kv_pool, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (!batch || !qkv || !kv_pool || !out) return RBKV_ERR_INVALID_ARG;
+  const rbkv_shape& s = *shape;
+  if (!same_shape(batch->shape, s)) return RBKV_ERR_INVALID_ARG;
+  if (batch->T < 0 || batch->T > s.max_tokens) return RBKV_ERR_INVALID_ARG;
+  size_t need = 0;
+  if ((st = rbkv_workspace_bytes(shape, batch, &need)) != RBKV_OK) return st;
+  if (workspace_bytes < need || (need > 0 && !workspace)) return RBKV_ERR_WORKSPACE;
+  if (batch->T == 0) return RBKV_OK;
+  const size_t e = elem_bytes(s);
+  const size_t qkv_bytes = (size_t)batch->T * (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * e;
+  const size_t pool_bytes = (size_t)s.num_blocks * 2 * s.n_kv_heads * s.block_size * s.head_dim * e;
+  const size_t out_bytes = (size_t)batch->T * s.n_q_heads * s.head_dim * e;
+  if ((st = check_device(qkv, qkv_bytes)) != RBKV_OK) return st;
+  if ((st = check_device(kv_pool, pool_bytes)) != RBKV_OK) return st;
+  if ((st = check_device(out, out_bytes)) != RBKV_OK) return st;
+  if (need > 0 && (st = check_device(workspace, need)) != RBKV_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t err = hipSuccess;
+  if (batch->n_prefill_items > 0) err = launch_prefill(s, *batch, qkv, kv_pool, out, hs);
+  if (err == hipSuccess && batch->n_decode_items > 0)
+    err = launch_decode(s, *batch, qkv, kv_pool, out, (float*)workspace, hs);
+  if (err == hipSuccess && batch->n_combine_items > 0)
+    err = launch_combine(s, *batch, (const float*)workspace, out, hs);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
+}  // extern "C"

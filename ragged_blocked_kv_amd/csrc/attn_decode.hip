@@ -1,0 +1,284 @@
+// Split-K streaming attention on the vector ALUs.  One 64-lane wavefront per work item
+// (token, kv head, split): it streams the split's keys in tiles of 64 (one key per lane
+// for Q.K, lanes spread over head-dim columns for P.V), keeps a running max and sum per
+// query head (online softmax with wavefront max reductions), and writes either the
+// finished output or an unnormalised partial (m, l, acc) for the combine kernel.
+//
+// All G query heads of a kv group share one pass over the keys (grouped-query reuse).
+// Tiles are fetched with coalesced 16-byte loads (each instruction covers whole rows of
+// one block) and K is staged through LDS with an XOR swizzle so that the transposed
+// one-row-per-lane reads are free of bank conflicts.  Used for single-token decodes
+// (split-K over long histories) and, in float32, for every token of a chunk.
+//
+// Blocked flash attention over per-head work atoms with an output scratch:
+// "DeepSpeed Inference v2 source tour", section "Ragged batches: packing a whole server
+// into four tensors"; FlashAttention-2-style integration: "DeepSpeed-Inference and
+// DeepSpeed-MII", section 10.3.
+#include "rbkv_device.h"
+#include "rbkv_internal.h"
+
+namespace rbkv {
+namespace {
+
+template <typename T, int D>
+struct DecGeom {
+  static constexpr int RB = D * (int)sizeof(T);  // bytes per key row
+  static constexpr int CPR = RB / 16;            // 16-byte chunks per row
+  static constexpr int KPI = 64 / CPR;           // keys per load instruction
+  static constexpr int NI = CPR;                 // load instructions per 64-key tile
+  static constexpr int VW = 16 / (int)sizeof(T); // elements per chunk
+};
+
+// Swizzled chunk slot of (row, chunk) in the LDS key tile.  Rows are CPR chunks long;
+// the XOR spreads 16 consecutive rows over 16 distinct 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int kslot(int row, int c) {
+  constexpr int SH = CPR >= 16 ? 0 : (CPR == 8 ? 1 : 2);
+  const int swz = CPR >= 16 ? (row & 15) : ((row >> SH) & (CPR - 1));
+  return row * CPR + (c ^ swz);
+}
+
+// The bf16 pair reinterpretation goes through a by-value word: a bit cast applied
+// directly to a vector-element lvalue (q.y, ...) is lowered as a read of element 0.
+__device__ __forceinline__ bf16x2v as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2v, w); }
+
+__device__ __forceinline__ float dot_chunk(u32x4 q, u32x4 k, float acc, bf16_t) {
+  const uint32_t q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
+  const uint32_t k0 = k.x, k1 = k.y, k2 = k.z, k3 = k.w;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q0), as_bf16x2(k0), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q1), as_bf16x2(k1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q2), as_bf16x2(k2), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q3), as_bf16x2(k3), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float dot_chunk(u32x4 q, u32x4 k, float acc, float) {
+  acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+  acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+  acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+  acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  return acc;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack_chunk(u32x4 v, float* f);
+template <>
+__device__ __forceinline__ void unpack_chunk<bf16_t>(u32x4 v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack_chunk<float>(u32x4 v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack_chunk(const float* f);
+template <>
+__device__ __forceinline__ u32x4 pack_chunk<bf16_t>(const float* f) {
+  u32x4 r;
+  r.x = pack_bf16x2(f[0], f[1]); r.y = pack_bf16x2(f[2], f[3]);
+  r.z = pack_bf16x2(f[4], f[5]); r.w = pack_bf16x2(f[6], f[7]);
+  return r;
+}
+template <>
+__device__ __forceinline__ u32x4 pack_chunk<float>(const float* f) {
+  u32x4 r;
+  r.x = __float_as_uint(f[0]); r.y = __float_as_uint(f[1]);
+  r.z = __float_as_uint(f[2]); r.w = __float_as_uint(f[3]);
+  return r;
+}
+
+template <typename T, int D, int GMAX>
+__global__ __launch_bounds__(64) void decode_attn_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ pool, T* __restrict__ out,
+    float* __restrict__ ws, const int4* __restrict__ work, const int32_t* __restrict__ tok2seq,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ block_off,
+    const int32_t* __restrict__ block_ids, int32_t Hq, int32_t Hkv, int32_t G, int32_t bs,
+    int32_t split_tiles, float scale_log2) {
+  using Gm = DecGeom<T, D>;
+  constexpr int CPR = Gm::CPR, KPI = Gm::KPI, NI = Gm::NI, VW = Gm::VW;
+  __shared__ u32x4 ktile[64 * CPR];
+  __shared__ u32x4 qs[GMAX * CPR];
+  __shared__ float ps[64 * GMAX];
+
+  const int lane = threadIdx.x;
+  const int4 w = work[blockIdx.x];
+  const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
+  const int32_t seq = tok2seq[token];
+  const int32_t nkeys = pos[token] + 1;
+  const int32_t tiles_total = (nkeys + 63) >> 6;
+  const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
+  const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
+  const int32_t key_end = min(nkeys, t_end * 64);
+  const int32_t* bids = block_ids + block_off[seq];
+  const size_t head_stride = (size_t)bs * D;          // one (block, kv, head) slab
+  const size_t v_off = (size_t)Hkv * head_stride;     // keys -> values of the same block
+
+  // Query rows of the group's G heads into LDS.
+  const int32_t row_elems = (Hq + 2 * Hkv) * D;
+  const T* qrow = qkv + (size_t)token * row_elems + (size_t)kvh * G * D;
+  for (int u = lane; u < G * CPR; u += 64) qs[u] = ld16(qrow + (size_t)(u / CPR) * D + (u % CPR) * VW);
+
+  float m[GMAX], lsum[GMAX], o[GMAX][VW];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    m[h] = -INFINITY;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) o[h][e] = 0.f;
+  }
+  const int cl = lane % CPR;  // chunk column this lane loads / accumulates
+  const int kg = lane / CPR;  // key sub-row within a load instruction
+
+  for (int32_t tt = t_begin; tt < t_end; ++tt) {
+    const int32_t key0 = tt * 64;
+    u32x4 kreg[NI], vreg[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int32_t key = key0 + i * KPI + kg;
+      kreg[i] = u32x4{0, 0, 0, 0};
+      vreg[i] = u32x4{0, 0, 0, 0};
+      if (key < key_end) {
+        const int64_t blk = bids[key / bs];
+        const T* src = pool + (size_t)(blk * 2 * Hkv + kvh) * head_stride +
+                       (size_t)(key % bs) * D + cl * VW;
+        kreg[i] = ld16(src);
+        vreg[i] = ld16(src + v_off);
+      }
+    }
+    __syncthreads();  // previous tile's LDS readers are done
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ktile[kslot<CPR>(i * KPI + kg, cl)] = kreg[i];
+    __syncthreads();
+
+    // Scores: lane = key.
+    float s[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) s[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+      const u32x4 kc = ktile[kslot<CPR>(lane, c)];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h < G) s[h] = dot_chunk(qs[h * CPR + c], kc, s[h], T{});
+    }
+    const bool valid = key0 + lane < key_end;
+    float alpha[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < G) {
+        const float sc = valid ? s[h] * scale_log2 : -INFINITY;
+        const float mn = fmaxf(m[h], wave_max(sc));
+        alpha[h] = exp2f(m[h] - mn);
+        m[h] = mn;
+        const float pe = exp2f(sc - mn);
+        lsum[h] = lsum[h] * alpha[h] + pe;
+        ps[lane * GMAX + h] = pe;
+      }
+    }
+    __syncthreads();
+
+    // P.V: lane accumulates VW columns over keys i*KPI + kg.
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+      if (h < G) {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) o[h][e] *= alpha[h];
+      }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float v[VW];
+      unpack_chunk<T>(vreg[i], v);
+      const float* pk = ps + (i * KPI + kg) * GMAX;
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h < G) {
+          const float ph = pk[h];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) o[h][e] = fmaf(ph, v[e], o[h][e]);
+        }
+    }
+  }
+
+  // Reduce over the lanes that share a chunk column, and the row sums over all lanes.
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < G) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+#pragma unroll
+        for (int off = CPR; off < 64; off <<= 1) o[h][e] += __shfl_xor(o[h][e], off, 64);
+      }
+      lsum[h] = wave_sum(lsum[h]);
+    }
+  }
+  if (slot < 0) {
+    if (lane < CPR) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h < G) {
+          const float inv = 1.f / lsum[h];
+          float r[VW];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) r[e] = o[h][e] * inv;
+          st16(out + ((size_t)token * Hq + (size_t)kvh * G + h) * D + cl * VW, pack_chunk<T>(r));
+        }
+    }
+  } else {
+    float* part = ws + (size_t)slot * G * (D + 2);
+    if (lane == 0) {
+      for (int h = 0; h < G; ++h) {
+        part[h] = m[h];
+        part[G + h] = lsum[h];
+      }
+    }
+    if (lane < CPR) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h < G) {
+          float* dst = part + 2 * G + (size_t)h * D + cl * VW;
+#pragma unroll
+          for (int e = 0; e < VW; ++e) dst[e] = o[h][e];
+        }
+    }
+  }
+}
+
+template <typename T, int D, int GMAX>
+hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
+                    void* out, float* ws, hipStream_t stream) {
+  const int G = s.n_q_heads / s.n_kv_heads;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL((decode_attn_kernel<T, D, GMAX>), dim3(b.n_decode_items), dim3(64), 0,
+                     stream, (const T*)qkv, (const T*)pool, (T*)out, ws,
+                     (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
+                     b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
+                     scale_log2);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
+                    void* out, float* ws, hipStream_t stream) {
+  const int G = s.n_q_heads / s.n_kv_heads;
+  if (G <= 1) return launch_t<T, D, 1>(s, b, qkv, pool, out, ws, stream);
+  if (G <= 2) return launch_t<T, D, 2>(s, b, qkv, pool, out, ws, stream);
+  if (G <= 4) return launch_t<T, D, 4>(s, b, qkv, pool, out, ws, stream);
+  if (G <= 8) return launch_t<T, D, 8>(s, b, qkv, pool, out, ws, stream);
+  return launch_t<T, D, 16>(s, b, qkv, pool, out, ws, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                         const void* pool, void* out, float* ws, hipStream_t stream) {
+  const bool bf = s.dtype == RBKV_DTYPE_BF16;
+  if (s.head_dim == 128)
+    return bf ? launch_g<bf16_t, 128>(s, b, qkv, pool, out, ws, stream)
+              : launch_g<float, 128>(s, b, qkv, pool, out, ws, stream);
+  return bf ? launch_g<bf16_t, 64>(s, b, qkv, pool, out, ws, stream)
+            : launch_g<float, 64>(s, b, qkv, pool, out, ws, stream);
+}
+
+}  // namespace rbkv

@@ -1,0 +1,76 @@
+// Device-side helpers for the gfx950 kernels: storage types, conversions, 16-byte
+// vector access and wavefront reductions (64 lanes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rbkv {
+
+// bfloat16 is carried as its 16-bit pattern.
+struct bf16_t {
+  uint16_t bits;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bfloat16 pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_f32(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne_f32(lo) | (bf16_rne_f32(hi) << 16);
+}
+
+// float64 -> bfloat16 pattern, round to nearest even in one step from binary64: drop
+// the low 45 fraction bits with RNE, the result is exact in binary32.
+__device__ __forceinline__ uint16_t bf16_rne_f64(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  u = (u + ((1ull << 44) - 1ull) + ((u >> 45) & 1ull)) & ~((1ull << 45) - 1ull);
+  const float f = (float)__longlong_as_double((long long)u);
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// Storage traits: element <-> float32/float64 and how many elements fill 16 bytes.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int VW = 4;
+  __device__ static __forceinline__ double to_f64(float v) { return (double)v; }
+  __device__ static __forceinline__ float from_f64(double v) { return (float)v; }
+};
+template <>
+struct Elem<bf16_t> {
+  static constexpr int VW = 8;
+  __device__ static __forceinline__ double to_f64(bf16_t v) {
+    return (double)__uint_as_float((uint32_t)v.bits << 16);
+  }
+  __device__ static __forceinline__ bf16_t from_f64(double v) { return bf16_t{bf16_rne_f64(v)}; }
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace rbkv

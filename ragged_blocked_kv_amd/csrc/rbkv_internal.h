@@ -1,0 +1,136 @@
+// Internal definitions shared by the host side of librbkv and its gfx950 kernels:
+// work decomposition, metadata-buffer layout and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rbkv.h"
+
+namespace rbkv {
+
+// Keys per decode tile: one key per lane of a 64-wide wavefront.
+constexpr int KT = 64;
+// Query rows (tokens x heads of one kv group) per prefill workgroup: 4 waves x 32.
+constexpr int PF_ROWS = 128;
+constexpr int MAX_GROUP = 16;
+constexpr int MAX_SEQS_LIMIT = 2048;
+constexpr int MAX_TOKENS_LIMIT = 1 << 20;
+constexpr int MAX_BLOCKS_LIMIT = 1 << 26;
+// Decode split-K sizing: aim for about this many decode work items per batch.
+constexpr int64_t DECODE_TARGET_ITEMS = 16384;
+constexpr int MIN_SPLIT_TILES = 2;
+constexpr int MAX_SPLIT_TILES = 64;
+
+// Header of the staged batch (int32 words at the start of the staging area).
+enum HeaderWord {
+  H_S = 0, H_T, H_NBLK, H_SPLIT, H_HKV, H_MFMA, H_QTT, H_NDEC, H_NPRE, H_NPART, H_NCOMB,
+  HDR_INTS = 16
+};
+
+__host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tokens of one sequence per prefill workgroup: as many as fit PF_ROWS rows of G heads.
+__host__ __device__ inline int32_t q_tile_tokens(int32_t G) {
+  int32_t q = PF_ROWS / G;
+  return q < 1 ? 1 : q;
+}
+
+struct SeqPlan {
+  int32_t dec_items;   // decode work items (token, kv head, split)
+  int32_t pre_items;   // prefill work items (q tile, kv head)
+  int32_t partials;    // split-K partial slots
+  int32_t comb_items;  // combine items (token, kv head)
+  int32_t nsplit;      // splits per (token, kv head) for a single-token decode
+};
+
+// Work decomposition of one sequence.  Single-token decodes stream their keys in
+// splits of split_tiles 64-key tiles; chunks of several tokens either go to MFMA
+// tiles (bf16) or become one vector-ALU item per token and kv head (float32).
+__host__ __device__ inline SeqPlan plan_sequence(int32_t n, int32_t seen, int32_t Hkv,
+                                                 int32_t split_tiles, bool mfma_prefill,
+                                                 int32_t qtt) {
+  SeqPlan p{0, 0, 0, 0, 1};
+  if (n == 1) {
+    int32_t tiles = (int32_t)cdiv64((int64_t)seen + 1, KT);
+    int32_t ns = (int32_t)cdiv64(tiles, split_tiles);
+    p.nsplit = ns;
+    p.dec_items = Hkv * ns;
+    if (ns > 1) {
+      p.partials = Hkv * ns;
+      p.comb_items = Hkv;
+    }
+  } else if (mfma_prefill) {
+    p.pre_items = Hkv * (int32_t)cdiv64(n, qtt);
+  } else {
+    p.dec_items = Hkv * n;
+  }
+  return p;
+}
+
+// Capacities of the work lists for a shape (upper bounds over every valid batch).
+struct Caps {
+  int64_t dec, pre, comb;
+};
+inline Caps work_caps(const rbkv_shape& s) {
+  Caps c;
+  const int64_t tiles = cdiv64((int64_t)s.num_blocks * s.block_size, KT) + s.max_seqs;
+  c.dec = (int64_t)s.n_kv_heads * (tiles + s.max_tokens);
+  c.pre = (int64_t)s.n_kv_heads * (s.max_tokens + s.max_seqs);
+  c.comb = (int64_t)s.n_kv_heads * s.max_seqs;
+  return c;
+}
+
+// Device metadata buffer layout (byte offsets, each 256-byte aligned).  The staging
+// region (header, n_new, seen, flat block ids) is the image of the pinned host buffer.
+struct MetaLayout {
+  size_t staging, n_new, seen, block_ids, staging_bytes;
+  size_t cu, kv_len, block_off, tok2seq, pos, dec, pre, comb, total;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline MetaLayout meta_layout(const rbkv_shape& s) {
+  MetaLayout L;
+  size_t at = 0;
+  L.staging = 0;
+  L.n_new = HDR_INTS * 4;
+  L.seen = L.n_new + (size_t)s.max_seqs * 4;
+  L.block_ids = L.seen + (size_t)s.max_seqs * 4;
+  L.staging_bytes = L.block_ids + (size_t)s.num_blocks * 4;
+  at = align256(L.staging_bytes);
+  Caps c = work_caps(s);
+  L.cu = at;        at = align256(at + (size_t)(s.max_seqs + 1) * 4);
+  L.kv_len = at;    at = align256(at + (size_t)s.max_seqs * 4);
+  L.block_off = at; at = align256(at + (size_t)(s.max_seqs + 1) * 4);
+  L.tok2seq = at;   at = align256(at + (size_t)s.max_tokens * 4);
+  L.pos = at;       at = align256(at + (size_t)s.max_tokens * 4);
+  L.dec = at;       at = align256(at + (size_t)c.dec * 16);
+  L.pre = at;       at = align256(at + (size_t)c.pre * 16);
+  L.comb = at;      at = align256(at + (size_t)c.comb * 16);
+  L.total = at;
+  return L;
+}
+
+// Floats per split-K partial slot: m[G], l[G], acc[G][d].
+inline size_t partial_floats(int32_t G, int32_t d) { return (size_t)G * (d + 2); }
+
+// ---- kernel launchers (defined in the .hip files) ----
+
+hipError_t launch_meta_build(const int32_t* staging, int32_t* cu, int32_t* kv_len,
+                             int32_t* block_off, int32_t* tok2seq, int32_t* pos,
+                             int32_t* dec, int32_t* pre, int32_t* comb, int32_t block_size,
+                             int32_t max_seqs, hipStream_t stream);
+
+hipError_t launch_append_rotary(const rbkv_shape& s, const rbkv_batch& b, void* qkv,
+                                void* pool, double rope_base, hipStream_t stream);
+
+hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                         const void* pool, void* out, float* ws, hipStream_t stream);
+
+hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                          const void* pool, void* out, hipStream_t stream);
+
+hipError_t launch_combine(const rbkv_shape& s, const rbkv_batch& b, const float* ws,
+                          void* out, hipStream_t stream);
+
+}  // namespace rbkv

@@ -1,0 +1,97 @@
+"""Buffer plumbing around the C ABI for tests and benchmarks.
+
+``Engine`` owns (through PyTorch) the buffers one layer shape needs -- pinned host
+staging, device metadata, the split-K workspace -- and calls the three entry points on
+a stream.  It does no arithmetic of the method: every step runs in librbkv's kernels.
+It raises ``RbkvError`` on any non-OK status.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (Batch, Shape, blocked_kv_append_rotary, check, ragged_batch_finalize,
+               ragged_blocked_attention, rbkv_metadata_bytes, rbkv_workspace_bytes)
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class Engine:
+    def __init__(self, *, max_tokens, max_seqs, num_blocks, block_size, n_q_heads,
+                 n_kv_heads, head_dim, dtype, device="cuda"):
+        if not torch.cuda.is_available():
+            raise RuntimeError("Engine needs a HIP device")
+        self.shape = Shape.make(max_tokens=max_tokens, max_seqs=max_seqs, num_blocks=num_blocks,
+                                block_size=block_size, n_q_heads=n_q_heads,
+                                n_kv_heads=n_kv_heads, head_dim=head_dim, dtype=dtype)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        st, dev_b, host_b = rbkv_metadata_bytes(self.shape)
+        check(st, "rbkv_metadata_bytes")
+        self.dev_meta = torch.empty(dev_b, dtype=torch.uint8, device=self.device)
+        self.host_pinned = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
+        self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self.batch: Batch | None = None
+
+    @classmethod
+    def for_workload(cls, wl, device="cuda"):
+        return cls(max_tokens=wl.max_tokens, max_seqs=wl.max_seqs, num_blocks=wl.num_blocks,
+                   block_size=wl.block_size, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                   head_dim=wl.head_dim, dtype=wl.dtype, device=device)
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+    def stream(self, stream=None):
+        return torch.cuda.current_stream(self.device) if stream is None else stream
+
+    def finalize(self, n_new, seen, block_lists, stream=None) -> Batch:
+        st, b = ragged_batch_finalize(self.shape, n_new, seen, block_lists, self.host_pinned,
+                                      self.host_pinned.numel(), self.dev_meta,
+                                      self.dev_meta.numel(), self.stream(stream))
+        check(st, "ragged_batch_finalize")
+        st, need = rbkv_workspace_bytes(self.shape, b)
+        check(st, "rbkv_workspace_bytes")
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        self.batch = b
+        return b
+
+    def append_rotary(self, qkv, kv_pool, rope_base, stream=None, batch=None):
+        check(blocked_kv_append_rotary(self.shape, batch or self.batch, qkv, kv_pool, rope_base,
+                                       self.stream(stream)), "blocked_kv_append_rotary")
+
+    def attention(self, qkv, kv_pool, out, stream=None, batch=None):
+        b = batch or self.batch
+        check(ragged_blocked_attention(self.shape, b, qkv, kv_pool, out, self.workspace,
+                                       self.workspace.numel(), self.stream(stream)),
+              "ragged_blocked_attention")
+
+    def new_out(self, T=None):
+        T = self.batch.T if T is None else T
+        return torch.empty((T, self.shape.n_q_heads, self.shape.head_dim),
+                           dtype=self.torch_dtype, device=self.device)
+
+    def metadata(self, batch=None):
+        """Device metadata of a finalized batch copied to host int32 arrays."""
+        b = batch or self.batch
+        base = self.dev_meta.data_ptr()
+        u8 = self.dev_meta
+
+        def arr(ptr, n):
+            off = int(ptr) - base
+            return u8[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
+        S, T = b.S, b.T
+        return {
+            "cu_seqlens": arr(b.cu_seqlens, S + 1),
+            "seen": arr(b.seen, S),
+            "kv_len": arr(b.kv_len, S),
+            "block_offsets": arr(b.block_offsets, S + 1),
+            "block_ids": arr(b.block_ids, b.n_blocks_used),
+            "token_to_seq": arr(b.token_to_seq, T),
+            "pos": arr(b.pos, T),
+            "decode_work": arr(b.decode_work, 4 * b.n_decode_items).reshape(-1, 4),
+            "prefill_work": arr(b.prefill_work, 4 * b.n_prefill_items).reshape(-1, 4),
+            "combine_work": arr(b.combine_work, 4 * b.n_combine_items).reshape(-1, 4),
+        }

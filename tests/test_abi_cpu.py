@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports what include/rbkv.h declares, the
+size queries answer, and every argument error comes back as a status code before any
+HIP call (fake addresses are fine for that reason)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ragged_blocked_kv_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: validation fails before any use
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "rbkv.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", txt, flags=re.M)))
+
+
+def shape(**kw):
+    base = dict(max_tokens=64, max_seqs=8, num_blocks=32, block_size=16, n_q_heads=4,
+                n_kv_heads=2, head_dim=64, dtype="bf16")
+    base.update(kw)
+    return R.Shape.make(**base)
+
+
+def sizes(s):
+    st, d, h = R.rbkv_metadata_bytes(s)
+    assert st == R.OK
+    return d, h
+
+
+def finalize(s, n_new, seen, lists, **kw):
+    d, h = sizes(s)
+    args = dict(host_pinned=FAKE, host_pinned_bytes=h, dev_meta=FAKE, dev_meta_bytes=d)
+    args.update(kw)
+    return R.ragged_batch_finalize(s, n_new, seen, lists, args["host_pinned"],
+                                   args["host_pinned_bytes"], args["dev_meta"],
+                                   args["dev_meta_bytes"], None)
+
+
+def test_library_exports_every_declared_function():
+    fns = header_functions()
+    assert set(fns) == set(R.EXPORTED_SYMBOLS), fns
+    L = ctypes.CDLL(R.LIB_PATH)
+    for f in fns:
+        assert hasattr(L, f), f
+
+
+def test_status_strings():
+    for st in range(8):
+        assert R.status_string(st) and R.status_string(st) != "unknown status"
+    assert R.status_string(99) == "unknown status"
+
+
+def test_metadata_bytes_and_shape_support():
+    d, h = sizes(shape())
+    assert d > h > 0 and d % 256 == 0
+    # capacities scale the buffers
+    d2, h2 = sizes(shape(max_tokens=8192, max_seqs=256, num_blocks=20000))
+    assert d2 > d and h2 > h
+    assert h2 >= 4 * (16 + 2 * 256 + 20000)
+    for bad in [dict(head_dim=96), dict(head_dim=256), dict(block_size=48), dict(block_size=8),
+                dict(dtype=7), dict(n_q_heads=6, n_kv_heads=4), dict(n_q_heads=64, n_kv_heads=2),
+                dict(max_seqs=4096)]:
+        assert R.rbkv_metadata_bytes(shape(**bad))[0] == R.ERR_UNSUPPORTED, bad
+    for bad in [dict(max_tokens=0), dict(num_blocks=0), dict(n_kv_heads=0)]:
+        assert R.rbkv_metadata_bytes(shape(**bad))[0] == R.ERR_INVALID_ARG, bad
+    for ok in [dict(head_dim=128), dict(block_size=128), dict(dtype="f32"),
+               dict(n_q_heads=14, n_kv_heads=2), dict(n_q_heads=32, n_kv_heads=2)]:
+        assert R.rbkv_metadata_bytes(shape(**ok))[0] == R.OK, ok
+
+
+def test_finalize_validation_errors():
+    s = shape()
+    lists = [np.array([0, 1, 2]), np.array([3])]
+    # capacity
+    assert finalize(s, [1] * 9, [0] * 9, [np.array([i]) for i in range(9)])[0] == R.ERR_CAPACITY
+    assert finalize(s, [40, 30], [0, 0], [np.arange(3), np.arange(3, 5)])[0] == R.ERR_CAPACITY
+    # bad counts
+    assert finalize(s, [0, 1], [0, 0], lists)[0] == R.ERR_INVALID_ARG
+    assert finalize(s, [1, 1], [-1, 0], lists)[0] == R.ERR_INVALID_ARG
+    # block lists: too short, out of range, duplicated (within and across sequences)
+    assert finalize(s, [20, 1], [13, 0], [np.array([0, 1]), np.array([3])])[0] == R.ERR_BLOCKS
+    assert finalize(s, [1, 1], [0, 0], [np.array([32]), np.array([3])])[0] == R.ERR_BLOCKS
+    assert finalize(s, [1, 1], [0, 0], [np.array([-1]), np.array([3])])[0] == R.ERR_BLOCKS
+    assert finalize(s, [1, 1], [0, 0], [np.array([4]), np.array([4])])[0] == R.ERR_BLOCKS
+    assert finalize(s, [20, 1], [0, 0], [np.array([4, 4]), np.array([5])])[0] == R.ERR_BLOCKS
+    # more blocks needed than the pool holds
+    assert finalize(s, [1], [600], [np.arange(40)])[0] == R.ERR_BLOCKS
+    # buffers: too small, null
+    d, h = sizes(s)
+    assert finalize(s, [1], [0], [np.array([0])], host_pinned_bytes=h - 1)[0] == R.ERR_WORKSPACE
+    assert finalize(s, [1], [0], [np.array([0])], dev_meta_bytes=d - 4)[0] == R.ERR_WORKSPACE
+    assert finalize(s, [1], [0], [np.array([0])], host_pinned=None)[0] == R.ERR_INVALID_ARG
+    assert finalize(s, [1], [0], [np.array([0])], dev_meta=None)[0] == R.ERR_INVALID_ARG
+    # unsupported shape comes first
+    st, _ = R.ragged_batch_finalize(shape(head_dim=80), [1], [0], [np.array([0])], FAKE, h,
+                                    FAKE, d, None)
+    assert st == R.ERR_UNSUPPORTED
+
+
+def test_finalize_null_lists_and_negative_S():
+    s = shape()
+    d, h = sizes(s)
+    st, _ = R.ragged_batch_finalize(s, [1], [0], [np.array([0])], FAKE, h, FAKE, d, None,
+                                    null_lists=True)
+    assert st == R.ERR_INVALID_ARG
+    st, _ = R.ragged_batch_finalize(s, [1], [0], [np.array([0])], FAKE, h, FAKE, d, None, S=-1)
+    assert st == R.ERR_INVALID_ARG
+
+
+def test_finalize_empty_batch_is_a_noop():
+    s = shape()
+    st, b = finalize(s, [], [], [])
+    assert st == R.OK and b.S == 0 and b.T == 0 and b.n_decode_items == 0
+    st, need = R.rbkv_workspace_bytes(s, b)
+    assert st == R.OK and need == 0
+    # T = 0: append and attention return OK without touching memory
+    assert R.blocked_kv_append_rotary(s, b, FAKE, FAKE, 1e4) == R.OK
+    assert R.ragged_blocked_attention(s, b, FAKE, FAKE, FAKE, None, 0) == R.OK
+
+
+def test_append_and_attention_validation():
+    s = shape()
+    b = R.Batch()
+    b.shape = s
+    b.T = 3
+    b.n_partials = 5
+    # null buffers
+    assert R.blocked_kv_append_rotary(s, b, None, FAKE, 1e4) == R.ERR_INVALID_ARG
+    assert R.ragged_blocked_attention(s, b, FAKE, None, FAKE, FAKE, 1 << 20) == R.ERR_INVALID_ARG
+    # batch built for another shape
+    other = shape(head_dim=128)
+    assert R.blocked_kv_append_rotary(other, b, FAKE, FAKE, 1e4) == R.ERR_INVALID_ARG
+    assert R.ragged_blocked_attention(other, b, FAKE, FAKE, FAKE, FAKE, 1 << 20) == \
+        R.ERR_INVALID_ARG
+    # workspace: 5 partial slots of G * (d + 2) floats
+    st, need = R.rbkv_workspace_bytes(s, b)
+    assert st == R.OK and need == 5 * 2 * (64 + 2) * 4
+    assert R.ragged_blocked_attention(s, b, FAKE, FAKE, FAKE, FAKE, need - 1) == R.ERR_WORKSPACE
+    assert R.ragged_blocked_attention(s, b, FAKE, FAKE, FAKE, None, need) == R.ERR_WORKSPACE
+    # T beyond capacity is a corrupted batch
+    b.T = 65
+    assert R.blocked_kv_append_rotary(s, b, FAKE, FAKE, 1e4) == R.ERR_INVALID_ARG
+
+
+def test_valid_call_without_gpu_reports_pointer_kind():
+    """With every argument valid the first HIP call is the pointer-kind check; on a
+    machine without a GPU (or with fake addresses) it fails as DEVICE_PTR or HIP, never
+    as a crash."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the GPU tests cover real buffers")
+    s = shape()
+    st, _ = finalize(s, [20, 1], [5, 3], [np.array([0, 1]), np.array([3])])
+    assert st in (R.ERR_DEVICE_PTR, R.ERR_HIP)
