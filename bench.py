@@ -1,0 +1,263 @@
+"""Throughput of one pass of the ragged-attention hot path on one MI355X.
+
+A step is one pass over one batch with every input already resident in HBM: the device
+metadata build (``ragged_batch_rebuild``), the rotary append
+(``blocked_kv_append_rotary``) and the attention (``ragged_blocked_attention``, issued as
+its prefill, decode and combine phases so that each kernel is timed with HIP events on
+the stream it runs on).  The batch is the full-budget mixed batch: 8192 new tokens over
+256 sequences (16 prefill chunks of 256..512 tokens and 240 decodes, seen ~ U[0, 8192]),
+GQA 32 query / 8 kv heads, head dim 128, 64-token blocks, bf16.  The host half of
+``ragged_batch_finalize`` (validation, packing, the small host-to-device upload) runs once
+before the timed region and is reported separately.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, TFLOP/s
+DEFAULT_WORKLOAD = "full8192_gqa4"
+PHASES = ("rebuild", "append", "prefill", "decode", "combine")
+
+
+def algorithmic_work(wl):
+    """Bytes each kernel must move and flops the prefill must do (no padding, no
+    partials, no metadata)."""
+    e = wl.elem_bytes
+    Hq, Hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    n = wl.n_new.astype(np.int64)
+    s = wl.seen.astype(np.int64)
+    L = n + s
+    dec = n == 1
+    chunk = ~dec
+    return {
+        "decode_bytes": float(e * (2 * Hkv * d * L[dec].sum() + 2 * Hq * d * dec.sum())),
+        "prefill_bytes": float(e * (2 * Hkv * d * L[chunk].sum() + 2 * Hq * d * n[chunk].sum())),
+        "prefill_flops": float(4 * d * Hq * (n[chunk] * s[chunk] +
+                                             n[chunk] * (n[chunk] + 1) // 2).sum()),
+        "attention_bytes": float(e * (2 * Hkv * d * L.sum() + 2 * Hq * d * n.sum())),
+        "append_bytes": float(e * d * n.sum() * (2 * (Hq + Hkv) + 2 * Hkv + Hkv)),
+    }
+
+
+def kernel_source_digest(name):
+    p = os.path.join(ROOT, "ragged_blocked_kv_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current source of that kernel (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{kernel_file}:{workload}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_digest(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, qkv_cpu, hist_fn, budget_s):
+    """The oracle as it stands, on a bounded sample of the same batch: sequences in a
+    seeded order (chunks and decodes interleaved), each through the oracle's append and
+    attention on a sub-pool holding its own blocks, until the time budget is spent."""
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    rng = np.random.default_rng(2024)
+    chunks = [int(i) for i in rng.permutation(np.nonzero(wl.n_new > 1)[0])]
+    decs = [int(i) for i in rng.permutation(np.nonzero(wl.n_new == 1)[0])]
+    order = []
+    while chunks or decs:
+        if chunks:
+            order.append(chunks.pop())
+        order.extend(decs[:15])
+        decs = decs[15:]
+    cu = np.concatenate([[0], np.cumsum(wl.n_new)])
+    qkv_np = qkv_cpu
+    done_tok, done_seq, n_chunks, spent = 0, 0, 0, 0.0
+    for i in order:
+        nb = -(-(int(wl.seen[i]) + int(wl.n_new[i])) // wl.block_size)
+        sub_pool = hist_fn(i, nb)  # input staging, not timed
+        t0 = time.perf_counter()
+        m1 = O.batch_metadata([wl.n_new[i]], [wl.seen[i]], [np.arange(nb, dtype=np.int32)],
+                              wl.block_size)
+        q, p = O.append_rotary(qkv_np[cu[i]:cu[i + 1]], sub_pool, m1, wl.n_q_heads,
+                               wl.n_kv_heads, wl.block_size, wl.rope_base, wl.dtype)
+        O.ragged_attention(q, p, m1, wl.n_q_heads, wl.n_kv_heads, wl.block_size, wl.dtype)
+        spent += time.perf_counter() - t0
+        done_tok += int(wl.n_new[i])
+        done_seq += 1
+        n_chunks += int(wl.n_new[i] > 1)
+        if spent >= budget_s:
+            break
+    return {
+        "value": done_tok / spent,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done_seq} of {wl.S} sequences of {wl.name} ({n_chunks} prefill chunks, "
+                   f"{done_seq - n_chunks} decodes, {done_tok} of {wl.T} tokens): float64 "
+                   f"oracle append + attention, {spent:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(shard by heads or by sequences and run one process per GPU instead)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from ragged_blocked_kv_amd import PHASE_COMBINE, PHASE_DECODE, PHASE_PREFILL
+    from ragged_blocked_kv_amd.runtime import Engine
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.make_workload(args.workload)
+    eng = Engine.for_workload(wl, device=dev)
+    qkv_cpu = W.make_qkv(wl)
+    qkv = qkv_cpu.to(dev)
+    pool = W.make_pool_history(wl, device=dev)
+    out = torch.empty((wl.T, wl.n_q_heads, wl.head_dim), dtype=qkv.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # Host half of finalize (validation, packing, upload): once, outside the timed region.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    eng.finalize(wl.n_new, wl.seen, wl.block_lists, stream=stream)
+    torch.cuda.synchronize()
+    finalize_us = (time.perf_counter() - t0) * 1e6
+
+    # CPU-baseline inputs: the pool history of the sampled sequences, copied before the
+    # first append overwrites this pass's slots.
+    hist = {}
+    if not args.no_cpu_baseline:
+        nb = [-(-(int(a) + int(b)) // wl.block_size) for a, b in zip(wl.n_new, wl.seen)]
+        for i in range(wl.S):
+            ids = torch.as_tensor(wl.block_lists[i][:nb[i]].astype(np.int64), device=dev)
+            blk = pool.index_select(0, ids).cpu()
+            hist[i] = blk.view(torch.int16).numpy().view(np.uint16) if wl.dtype == "bf16" \
+                else blk.numpy()
+
+    def step(ev=None):
+        def mark(k):
+            if ev is not None:
+                ev[k].record(stream)
+        mark(0)
+        eng.rebuild(stream=stream)
+        mark(1)
+        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
+        mark(2)
+        eng.attention_phase(PHASE_PREFILL, qkv, pool, out, stream=stream)
+        mark(3)
+        eng.attention_phase(PHASE_DECODE, qkv, pool, out, stream=stream)
+        mark(4)
+        eng.attention_phase(PHASE_COMBINE, qkv, pool, out, stream=stream)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    phase_ms = {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
+                                  for k in range(args.steps)]))
+                for j, p in enumerate(PHASES)}
+    ms_per_step = wall * 1e3 / args.steps
+    work = algorithmic_work(wl)
+    dec_gbs = work["decode_bytes"] / (phase_ms["decode"] * 1e-3) / 1e9 if phase_ms["decode"] else 0
+    pre_tfs = work["prefill_flops"] / (phase_ms["prefill"] * 1e-3) / 1e12 \
+        if phase_ms["prefill"] else 0
+    if phase_ms["prefill"] >= phase_ms["decode"]:
+        roof = {"kernel": "prefill_attn_kernel", "bound": "mfma", "achieved": pre_tfs,
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": pre_tfs / MFMA_BF16_PEAK_TFS,
+                "traffic": measured_traffic("attn_prefill.hip", wl.name),
+                "per_launch": {"flops": work["prefill_flops"], "us": phase_ms["prefill"] * 1e3}}
+    else:
+        roof = {"kernel": "decode_attn_kernel", "bound": "hbm", "achieved": dec_gbs,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                "traffic": measured_traffic("attn_decode.hip", wl.name),
+                "per_launch": {"bytes": work["decode_bytes"], "us": phase_ms["decode"] * 1e3}}
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(wl, qkv_cpu.view(torch.int16).numpy().view(np.uint16)
+                            if wl.dtype == "bf16" else qkv_cpu.numpy(),
+                            lambda i, nb: hist[i], args.cpu_seconds)
+
+    attn_ms = phase_ms["prefill"] + phase_ms["decode"] + phase_ms["combine"]
+    rec = {
+        "metric": "ragged attention tokens/s on 1 GPU + % peak HBM GB/s (decode) / % MFMA (prefill)",
+        "value": wl.T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": f"{wl.S} sequences, {wl.T} new tokens "
+                     f"({int((wl.n_new > 1).sum())} prefill chunks, {int((wl.n_new == 1).sum())} decodes)",
+            "heads": f"{wl.n_q_heads} q / {wl.n_kv_heads} kv",
+            "head_dim": wl.head_dim,
+            "block_size": wl.block_size,
+            "kv_pool_blocks": wl.num_blocks,
+            "step": "metadata rebuild + rotary append + attention (prefill, decode, combine)",
+        },
+        "roofline": roof,
+        "cpu_baseline": base,
+        "phases_us": {p: round(v * 1e3, 2) for p, v in phase_ms.items()},
+        "attention_only": {
+            "tokens_per_s": wl.T / (attn_ms * 1e-3),
+            "hbm_frac_decode": dec_gbs / HBM_PEAK_GBS,
+            "mfma_frac_prefill": pre_tfs / MFMA_BF16_PEAK_TFS,
+            "attention_algorithmic_GBs": work["attention_bytes"] / (attn_ms * 1e-3) / 1e9,
+        },
+        "finalize_host_and_upload_us": round(finalize_us, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,6 +73,14 @@ enum {
 
 enum { RBKV_DTYPE_F32 = 0, RBKV_DTYPE_BF16 = 1 };
 
+/* Phases of ragged_blocked_attention (see ragged_blocked_attention_phase). */
+enum {
+  RBKV_PHASE_ALL = 0,     /* everything below, in this order */
+  RBKV_PHASE_PREFILL = 1, /* multi-token chunks (bf16: matrix cores) */
+  RBKV_PHASE_DECODE = 2,  /* single-token decodes, split-K (and float32 chunks) */
+  RBKV_PHASE_COMBINE = 3  /* log-sum-exp merge of the split-K partials */
+};
+
 /* Static shape of one attention layer and its KV pool, plus the batch capacities.
  * Supported: head_dim in {64, 128}; block_size in {16, 32, 64, 128};
  * n_q_heads = G * n_kv_heads with 1 <= G <= 16; 1 <= max_seqs <= 2048;
@@ -130,14 +138,15 @@ const char* rbkv_status_string(rbkv_status status);
 
 /* Sizes of the two caller-owned buffers ragged_batch_finalize needs for `shape`:
  * device metadata (dev_bytes) and page-locked host staging (host_pinned_bytes, from
- * hipHostMalloc).  They are the "preallocated host buffers" and device tensors of the
- * ragged batch ("DeepSpeed Inference v2 source tour", section "Ragged batches").
+ * hipHostMalloc).  They play the part of the host buffers that the pages' batch wrapper
+ * fills ahead of time and of its device tensors ("DeepSpeed Inference v2 source tour",
+ * section "Ragged batches").
  * Either output pointer may be NULL.  Pure host computation. */
 rbkv_status rbkv_metadata_bytes(const rbkv_shape* shape, size_t* dev_bytes,
                                 size_t* host_pinned_bytes);
 
 /* Device workspace ragged_blocked_attention needs for `batch` (split-K partial
- * results, the "out scratch" handed to the blocked attention kernel in the same
+ * results; the scratch output the blocked attention kernel is handed in the same
  * section).  0 when no decode is split.  Pure host computation. */
 rbkv_status rbkv_workspace_bytes(const rbkv_shape* shape, const rbkv_batch* batch,
                                  size_t* bytes);
@@ -166,6 +175,14 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
                                   size_t host_pinned_bytes, void* dev_meta,
                                   size_t dev_meta_bytes, void* stream, rbkv_batch* out);
 
+/* Re-run the device half of ragged_batch_finalize: rebuild the batch's device metadata
+ * from the staged copy already in its metadata buffer, with no host packing and no
+ * transfer.  For a batch whose metadata buffer was reused or overwritten, or to time
+ * the device work alone.  `batch` must come from a successful finalize with the same
+ * shape and metadata buffer.  Errors: INVALID_ARG, HIP.  Enqueues one kernel. */
+rbkv_status ragged_batch_rebuild(const rbkv_shape* shape, const rbkv_batch* batch,
+                                 void* stream);
+
 /* Rotary position embedding and KV append for one layer.
  *   qkv       device [T][Hq + 2*Hkv][d]; the Q heads are rotated IN PLACE, K and V rows
  *             are left as they are.
@@ -193,6 +210,17 @@ rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* 
 rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
                                      const void* qkv, const void* kv_pool, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* One phase of ragged_blocked_attention (RBKV_PHASE_*), for callers that place other
+ * work between the phases or time them separately.  Running PREFILL, DECODE, COMBINE in
+ * this order on one stream is exactly ragged_blocked_attention; COMBINE reads what
+ * DECODE wrote to the workspace.  A phase with no work items returns OK without
+ * launching.  Errors: as ragged_blocked_attention, plus INVALID_ARG for an unknown
+ * phase. */
+rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_batch* batch,
+                                           int32_t phase, const void* qkv, const void* kv_pool,
+                                           void* out, void* workspace, size_t workspace_bytes,
+                                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,9 @@ import numpy as np
 __all__ = [
     "RbkvError", "Shape", "Batch", "lib", "status_string", "check",
     "rbkv_metadata_bytes", "rbkv_workspace_bytes", "ragged_batch_finalize",
-    "blocked_kv_append_rotary", "ragged_blocked_attention", "EXPORTED_SYMBOLS",
+    "blocked_kv_append_rotary", "ragged_blocked_attention", "ragged_batch_rebuild",
+    "ragged_blocked_attention_phase", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
+    "PHASE_DECODE", "PHASE_COMBINE",
     "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
     "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "DTYPE_F32", "DTYPE_BF16",
 ]
@@ -26,6 +28,7 @@ __all__ = [
 OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_BLOCKS, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 ERR_WORKSPACE, ERR_DEVICE_PTR, ERR_HIP = 5, 6, 7
 DTYPE_F32, DTYPE_BF16 = 0, 1
+PHASE_ALL, PHASE_PREFILL, PHASE_DECODE, PHASE_COMBINE = 0, 1, 2, 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librbkv.so")
 
@@ -34,8 +37,10 @@ EXPORTED_SYMBOLS = (
     "rbkv_metadata_bytes",
     "rbkv_workspace_bytes",
     "ragged_batch_finalize",
+    "ragged_batch_rebuild",
     "blocked_kv_append_rotary",
     "ragged_blocked_attention",
+    "ragged_blocked_attention_phase",
 )
 
 
@@ -93,6 +98,13 @@ def lib():
             ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, ctypes.POINTER(_P), _P,
             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
             ctypes.c_void_p, ctypes.POINTER(Batch)]
+        L.ragged_batch_rebuild.restype = ctypes.c_int32
+        L.ragged_batch_rebuild.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Batch),
+                                           ctypes.c_void_p]
+        L.ragged_blocked_attention_phase.restype = ctypes.c_int32
+        L.ragged_blocked_attention_phase.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_int32, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.blocked_kv_append_rotary.restype = ctypes.c_int32
         L.blocked_kv_append_rotary.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
@@ -184,3 +196,14 @@ def ragged_blocked_attention(shape: Shape, batch: Batch, qkv, kv_pool, out, work
     return lib().ragged_blocked_attention(ctypes.byref(shape), ctypes.byref(batch), _ptr(qkv),
                                           _ptr(kv_pool), _ptr(out), _ptr(workspace),
                                           int(workspace_bytes), _stream(stream))
+
+
+def ragged_batch_rebuild(shape: Shape, batch: Batch, stream=None) -> int:
+    return lib().ragged_batch_rebuild(ctypes.byref(shape), ctypes.byref(batch), _stream(stream))
+
+
+def ragged_blocked_attention_phase(shape: Shape, batch: Batch, phase: int, qkv, kv_pool, out,
+                                   workspace, workspace_bytes: int, stream=None) -> int:
+    return lib().ragged_blocked_attention_phase(
+        ctypes.byref(shape), ctypes.byref(batch), int(phase), _ptr(qkv), _ptr(kv_pool),
+        _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))

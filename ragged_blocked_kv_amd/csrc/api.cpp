@@ -72,6 +72,19 @@ rbkv_status check_pinned(const void* p) {
   return a.type == hipMemoryTypeHost ? RBKV_OK : RBKV_ERR_DEVICE_PTR;
 }
 
+rbkv_status launch_build(const rbkv_shape& s, char* dm, hipStream_t stream) {
+  const MetaLayout L = meta_layout(s);
+  if (launch_meta_build((const int32_t*)dm, (int32_t*)(dm + L.cu), (int32_t*)(dm + L.kv_len),
+                        (int32_t*)(dm + L.block_off), (int32_t*)(dm + L.tok2seq),
+                        (int32_t*)(dm + L.pos), (int32_t*)(dm + L.dec), (int32_t*)(dm + L.pre),
+                        (int32_t*)(dm + L.comb), s.block_size, s.max_seqs, stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
 bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
   return memcmp(&a, &b, sizeof(rbkv_shape)) == 0;
 }
@@ -251,16 +264,23 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
   }
-  if (launch_meta_build((const int32_t*)dm, (int32_t*)(dm + L.cu), (int32_t*)(dm + L.kv_len),
-                        (int32_t*)(dm + L.block_off), (int32_t*)(dm + L.tok2seq),
-                        (int32_t*)(dm + L.pos), (int32_t*)(dm + L.dec),
-                        (int32_t*)(dm + L.pre), (int32_t*)(dm + L.comb), s.block_size,
-                        s.max_seqs, hs_stream) != hipSuccess) {
-    (void)hipGetLastError();
-    return RBKV_ERR_HIP;
-  }
+  if ((st = launch_build(s, dm, hs_stream)) != RBKV_OK) return st;
   *out = b;
   return RBKV_OK;
+}
+
+rbkv_status ragged_batch_rebuild(const rbkv_shape* shape, const rbkv_batch* batch,
+                                 void* stream) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (!batch || !same_shape(batch->shape, *shape)) return RBKV_ERR_INVALID_ARG;
+  if (batch->S == 0) return RBKV_OK;
+  // The staging image sits at the start of the metadata buffer, just before n_new.
+  const MetaLayout L = meta_layout(*shape);
+  char* dm = (char*)batch->seen - L.seen;
+  if ((const char*)batch->cu_seqlens != dm + L.cu) return RBKV_ERR_INVALID_ARG;
+  if ((st = check_device(dm, L.total)) != RBKV_OK) return st;
+  return launch_build(*shape, dm, (hipStream_t)stream);
 }
 
 rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* batch,
@@ -286,12 +306,14 @@ rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* 
   return RBKV_OK;
 }
 
-rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
-                                     const void* qkv, const void* kv_pool, void* out,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_batch* batch,
+                                           int32_t phase, const void* qkv, const void* kv_pool,
+                                           void* out, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
   rbkv_status st = check_shape(shape);
   if (st != RBKV_OK) return st;
   if (!batch || !qkv || !kv_pool || !out) return RBKV_ERR_INVALID_ARG;
+  if (phase < RBKV_PHASE_ALL || phase > RBKV_PHASE_COMBINE) return RBKV_ERR_INVALID_ARG;
   const rbkv_shape& s = *shape;
   if (!same_shape(batch->shape, s)) return RBKV_ERR_INVALID_ARG;
   if (batch->T < 0 || batch->T > s.max_tokens) return RBKV_ERR_INVALID_ARG;
@@ -299,6 +321,13 @@ rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* 
   if ((st = rbkv_workspace_bytes(shape, batch, &need)) != RBKV_OK) return st;
   if (workspace_bytes < need || (need > 0 && !workspace)) return RBKV_ERR_WORKSPACE;
   if (batch->T == 0) return RBKV_OK;
+  const bool pre = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_PREFILL) &&
+                   batch->n_prefill_items > 0;
+  const bool dec = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_DECODE) &&
+                   batch->n_decode_items > 0;
+  const bool comb = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_COMBINE) &&
+                    batch->n_combine_items > 0;
+  if (!pre && !dec && !comb) return RBKV_OK;
   const size_t e = elem_bytes(s);
   const size_t qkv_bytes = (size_t)batch->T * (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * e;
   const size_t pool_bytes = (size_t)s.num_blocks * 2 * s.n_kv_heads * s.block_size * s.head_dim * e;
@@ -309,16 +338,23 @@ rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* 
   if (need > 0 && (st = check_device(workspace, need)) != RBKV_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t err = hipSuccess;
-  if (batch->n_prefill_items > 0) err = launch_prefill(s, *batch, qkv, kv_pool, out, hs);
-  if (err == hipSuccess && batch->n_decode_items > 0)
+  if (pre) err = launch_prefill(s, *batch, qkv, kv_pool, out, hs);
+  if (err == hipSuccess && dec)
     err = launch_decode(s, *batch, qkv, kv_pool, out, (float*)workspace, hs);
-  if (err == hipSuccess && batch->n_combine_items > 0)
+  if (err == hipSuccess && comb)
     err = launch_combine(s, *batch, (const float*)workspace, out, hs);
   if (err != hipSuccess) {
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
   }
   return RBKV_OK;
+}
+
+rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
+                                     const void* qkv, const void* kv_pool, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_ALL, qkv, kv_pool, out,
+                                        workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -10,7 +10,8 @@ from __future__ import annotations
 import torch
 
 from . import (Batch, Shape, blocked_kv_append_rotary, check, ragged_batch_finalize,
-               ragged_blocked_attention, rbkv_metadata_bytes, rbkv_workspace_bytes)
+               ragged_batch_rebuild, ragged_blocked_attention, ragged_blocked_attention_phase,
+               rbkv_metadata_bytes, rbkv_workspace_bytes)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -56,6 +57,16 @@ class Engine:
             self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         self.batch = b
         return b
+
+    def rebuild(self, stream=None, batch=None):
+        check(ragged_batch_rebuild(self.shape, batch or self.batch, self.stream(stream)),
+              "ragged_batch_rebuild")
+
+    def attention_phase(self, phase, qkv, kv_pool, out, stream=None, batch=None):
+        check(ragged_blocked_attention_phase(self.shape, batch or self.batch, phase, qkv,
+                                             kv_pool, out, self.workspace,
+                                             self.workspace.numel(), self.stream(stream)),
+              "ragged_blocked_attention_phase")
 
     def append_rotary(self, qkv, kv_pool, rope_base, stream=None, batch=None):
         check(blocked_kv_append_rotary(self.shape, batch or self.batch, qkv, kv_pool, rope_base,
