@@ -28,8 +28,12 @@ __device__ __forceinline__ uint32_t bf16_rne_f32(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+// Two floats -> packed bfloat16 pair (lo in bits 0..15), round to nearest even; one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne_f32(lo) | (bf16_rne_f32(hi) << 16);
+  const f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
 // float64 -> bfloat16 pattern, round to nearest even in one step from binary64: drop
