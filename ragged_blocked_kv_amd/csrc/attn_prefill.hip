@@ -6,17 +6,19 @@
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, keys x rows, K from LDS, Q held in registers)
 //   online softmax down each column (the lane owns one row: a column max is 16 register
 //                 maxima plus one exchange with the partner lane 32 away),
-//   O^T += V^T P^T (same instruction; P comes straight from the S^T accumulators, V from
-//                 a transposed LDS copy),
+//   O^T += V^T P^T (same instruction; P comes straight from the S^T accumulators, the
+//                 V^T fragments from transposing LDS reads, ds_read_b64_tr_b16),
 // over 64-key tiles, with the causal mask applied bottom-right (query at position p sees
 // keys 0..p, p = seen + offset in the chunk) and only on the tiles that need it.
 //
-// Pipeline: K/V tiles are double-buffered in LDS with one barrier per tile.  While a
-// tile is computed, the next tile sits in registers waiting to be stored and the one
-// after it is in flight from HBM; block ids are fetched one tile further ahead, so the
-// id -> address -> data chain never stalls a tile.  Work items are mapped onto block
-// indices so that the query tiles of one (sequence, kv head) run on the same XCD and
-// share its L2.
+// Data movement: K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+// no staging registers), double-buffered with one barrier per tile; the next tile is
+// in flight while the current one is computed, and block ids are fetched one tile
+// further ahead.  Each lane's source address is chosen so that the LDS image carries an
+// XOR swizzle: K fragments (16 consecutive rows, one 16-byte chunk each) and transposed
+// V reads (8 keys x 32 dims per instruction) are both free of bank conflicts.  Work
+// items are mapped onto block indices so that the query tiles of one (sequence,
+// kv head) run on the same XCD and share its L2.
 //
 // Dynamic SplitFuse chunks continuing a sequence with seen cached tokens:
 // "DeepSpeed-Inference and DeepSpeed-MII", sections 10.3 and 10.10; query-tile sizing per
@@ -28,33 +30,71 @@
 namespace rbkv {
 namespace {
 
-constexpr int PF_THREADS = 256;
+constexpr int PF_WAVES = PF_ROWS / 32;
+constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int STAGES = 4;  // K/V tiles resident in LDS: one computed, up to three in flight
 constexpr int N_XCD = 8;
-constexpr int VTS = 68;  // transposed-V row stride in bf16 elements (64 keys + pad, 8-byte aligned)
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// K tile: row = key (CPR 16-byte chunks); chunk c of row r sits at c ^ (r % 16)
+// (r / 2 % 8 for 8-chunk rows): the 16 rows of one fragment read hit 16 bank groups.
 template <int CPR>
-__device__ __forceinline__ int kslot(int row, int c) {
-  constexpr int SH = CPR >= 16 ? 0 : 1;
-  const int swz = CPR >= 16 ? (row & 15) : ((row >> SH) & (CPR - 1));
-  return row * CPR + (c ^ swz);
+__device__ __forceinline__ int kswz(int row) {
+  return CPR >= 16 ? (row & 15) : ((row >> 1) & 7);
+}
+// V tile: row = key; chunk u of row r sits at u ^ (4 * (r % 4)) (CPR = 16) or
+// u ^ (2 * (r % 4)) (CPR = 8): one transposing read (4 rows x 2 chunks per half-wave
+// pair) covers all 64 banks.
+template <int CPR>
+__device__ __forceinline__ int vswz(int row) {
+  return CPR >= 16 ? 4 * (row & 3) : 2 * (row & 3);
 }
 
 __device__ __forceinline__ bf16x8v as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8v, v); }
 
+// 2^x with one v_exp_f32: results below the normal range flush to 0, which only drops
+// softmax weights under 2^-126 of the running maximum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// HBM -> LDS without registers: lane l writes its 16 bytes at dst + 16*l (dst must be
+// wave-uniform).  Kept in a device function: used directly in a kernel template, the
+// builtin makes the host pass drop that kernel's launch stub.
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding (the LDS
+// DMA loads of later tiles stay in flight); expcnt and lgkmcnt are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int D>
-__global__ __launch_bounds__(PF_THREADS, 2) void prefill_attn_kernel(
+__global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_items,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
     int32_t Hkv, int32_t G, int32_t bs, float scale_log2) {
-  constexpr int CPR = D / 8;                // 16-byte chunks per key row
-  constexpr int RPI = PF_THREADS / CPR;     // key rows covered by one pass of the WG
-  constexpr int NP = 32 / RPI;              // adjacent key pairs per thread per tile
-  constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;                // 32-wide dim blocks of the output
-  __shared__ u32x4 Ks[2][64 * CPR];
-  __shared__ uint32_t Vt[2][D * VTS / 2];
+  constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  constexpr int TILE_CHUNKS = 64 * CPR;    // chunks per K (or V) tile
+  constexpr int NLD = TILE_CHUNKS / PF_THREADS;  // direct loads per thread per K (or V) tile
+  constexpr int LPT = 2 * NLD;             // vector-memory operations per thread per tile
+  constexpr int KSTEPS = D / 16;           // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;               // 32-wide dim blocks of the output
+  constexpr int MAXNB = 4;                 // blocks a 64-key tile can span (block size 16)
+  static_assert(NLD >= 1, "tile smaller than the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[STAGES][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[STAGES][64 * D];
 
   // XCD-aware mapping: block b runs on XCD b % 8; give each XCD a contiguous run of
   // items so that the query tiles of one (sequence, kv head) share an L2.
@@ -76,6 +116,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_attn_kernel(
   const int32_t n_keys = seen + q1;            // keys visible to the last token
   const int32_t ntile = (n_keys + 63) >> 6;
   const int32_t* bids = block_ids + block_off[seq];
+  const int32_t last_blk = (n_keys - 1) / bs;
   const size_t head_stride = (size_t)bs * D;
   const size_t v_off = (size_t)Hkv * head_stride;
   const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
@@ -101,51 +142,46 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_attn_kernel(
     for (int s = 0; s < KSTEPS; ++s) qb[s] = ld16(qr + 16 * s + 8 * hl);
   }
 
-  // Loader role: pair p of this thread covers keys 2*kp and 2*kp+1 of a tile, chunk c.
-  const int c_ld = tid % CPR;
-  int kp_ld[NP];
+  // Loader role: direct load i of this thread fills LDS chunk i*PF_THREADS + tid of a
+  // tile, which holds row (i*PF_THREADS + tid) / CPR and, after the swizzle, a chunk of
+  // that row.
+  int krow[NLD], kchk[NLD], vchk[NLD];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) kp_ld[p] = p * RPI + tid / CPR;
-
-  // Block id of each pair's keys for a tile (-1 past the end of the sequence).
-  auto fetch_ids = [&](int32_t t, int64_t* ids) {
+  for (int i = 0; i < NLD; ++i) {
+    const int pos = i * PF_THREADS + tid;
+    krow[i] = pos / CPR;
+    kchk[i] = (pos % CPR) ^ kswz<CPR>(krow[i]);
+    vchk[i] = (pos % CPR) ^ vswz<CPR>(krow[i]);
+  }
+  // Block ids of a tile: uniform across the workgroup, so they come through the scalar
+  // cache and never hold up the vector-memory queue that carries the tile data.
+  auto fetch_ids = [&](int32_t t, int32_t* ids) {
+    const int32_t b0 = min((t * 64) / bs, last_blk);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int32_t key = t * 64 + 2 * kp_ld[p];
-      ids[p] = (t < ntile && key < n_keys) ? (int64_t)bids[key / bs] : -1;
+    for (int j = 0; j < MAXNB; ++j) ids[j] = bids[min(b0 + j, last_blk)];
+  };
+  const size_t blk_stride = (size_t)2 * Hkv * head_stride;  // elements per pool block
+  auto issue_loads = [&](int32_t t, const int32_t* ids, int buf) {
+    if (bs >= 64 && t * 64 + 63 < n_keys) {
+      // The whole tile sits in one block: one uniform base, fixed per-thread offsets.
+      const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)((t * 64) % bs) * D;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint16_t* src = base + krow[i] * D;
+        load_lds16(src + kchk[i] * 8, Ks[buf] + (i * PF_THREADS + wave * 64) * 8);
+        load_lds16(src + v_off + vchk[i] * 8, Vs[buf] + (i * PF_THREADS + wave * 64) * 8);
+      }
+      return;
     }
-  };
-  u32x4 st_k[NP][2], st_v[NP][2];  // staged tile (registers)
-  auto issue_loads = [&](int32_t t, const int64_t* ids) {
+    const int32_t b0 = (t * 64) / bs;
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int32_t key = t * 64 + 2 * kp_ld[p] + j;
-        st_k[p][j] = u32x4{0, 0, 0, 0};
-        st_v[p][j] = u32x4{0, 0, 0, 0};
-        if (ids[p] >= 0 && key < n_keys) {
-          const uint16_t* src = pool_g + (size_t)(ids[p] * 2 * Hkv) * head_stride +
-                                (size_t)(key % bs) * D + c_ld * 8;
-          st_k[p][j] = ld16(src);
-          st_v[p][j] = ld16(src + v_off);
-        }
-      }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int kp = kp_ld[p];
-      Ks[buf][kslot<CPR>(2 * kp, c_ld)] = st_k[p][0];
-      Ks[buf][kslot<CPR>(2 * kp + 1, c_ld)] = st_k[p][1];
-      const u32x4 a = st_v[p][0], b = st_v[p][1];
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t lo = (j & 1) ? (aw[j >> 1] >> 16) : (aw[j >> 1] & 0xffffu);
-        const uint32_t hi = (j & 1) ? (bw[j >> 1] & 0xffff0000u) : (bw[j >> 1] << 16);
-        Vt[buf][((8 * c_ld + j) * VTS + 2 * kp) >> 1] = lo | hi;
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const int32_t key = min(t * 64 + krow[i], n_keys - 1);  // rows past the end: last key
+      const int jb = key / bs - b0;
+      const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
+      const uint16_t* src = pool_g + (size_t)id * blk_stride + (size_t)(key % bs) * D;
+      load_lds16(src + kchk[i] * 8, Ks[buf] + (i * PF_THREADS + wave * 64) * 8);
+      load_lds16(src + v_off + vchk[i] * 8, Vs[buf] + (i * PF_THREADS + wave * 64) * 8);
     }
   };
 
@@ -156,110 +192,128 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_attn_kernel(
     for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Prologue: tile 0 into LDS, tile 1 in flight, ids of tile 2 in flight.
-  int64_t ids_a[NP], ids_b[NP];
-  fetch_ids(0, ids_a);
-  fetch_ids(1, ids_b);
-  issue_loads(0, ids_a);
-  store_stage(0);
-  issue_loads(1, ids_b);
-  fetch_ids(2, ids_a);
-  __syncthreads();
+  // Transposing-read addresses of the V^T fragments (element offsets into a V tile):
+  // source lane 16g + 4j + r reads key kbase + 4(g/2) + j, dims 32d + 16(g%2) + 4r .. +4.
+  const int tg = lane >> 4, tj = (lane >> 2) & 3, trr = lane & 3;
+  const int vkey_in = 4 * (tg >> 1) + tj;                  // + kbase (multiple of 8)
+  const int vdim_in = 16 * (tg & 1) + 4 * trr;             // + 32d
+
+  // Prologue: tiles 0 .. STAGES-2 in flight, ids of tile STAGES-1 fetched.
+  int32_t ids[MAXNB];
+  fetch_ids(0, ids);
+#pragma unroll
+  for (int j = 0; j < STAGES - 1; ++j) {
+    if (j < ntile) issue_loads(j, ids, j);
+    fetch_ids(j + 1, ids);
+  }
 
   for (int32_t t = 0; t < ntile; ++t) {
-    const int buf = t & 1;
+    const int buf = t % STAGES;
+    // Tile t has landed once at most (tiles issued after it) * LPT loads are pending.
+    const int32_t later = min(STAGES - 2, ntile - 1 - t);
+    if (later >= 2) wait_vmcnt<2 * LPT>();
+    else if (later == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // everyone's part of tile t is in; buffer (t - 1) % STAGES is free
+    if (t + STAGES - 1 < ntile) {
+      issue_loads(t + STAGES - 1, ids, (t + STAGES - 1) % STAGES);
+      fetch_ids(t + STAGES, ids);
+    }
     const int32_t key0 = t * 64;
-    if (wave_active && key0 <= pmax) {
-      // S^T = K Q^T for keys key0 .. key0+63 (two 32-key blocks).
-      f32x16 sacc[2];
+    if (!wave_active || key0 > pmax) continue;  // nothing of this tile is visible
+    // S^T = K Q^T for keys key0 .. key0+63 (two 32-key blocks, their accumulation
+    // chains interleaved so consecutive MFMAs are independent).
+    f32x16 sacc[2];
+    {
+      u32x4 a[2][KSTEPS];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int krow_r = 32 * kb + col;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+          a[kb][s] = *(const u32x4*)(Ks[buf] +
+                                     (krow_r * CPR + ((2 * s + hl) ^ kswz<CPR>(krow_r))) * 8);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const u32x4 a = Ks[buf][kslot<CPR>(32 * kb + col, 2 * s + hl)];
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qb[s]),
-                                                            sacc[kb], 0, 0, 0);
-        }
       }
-      // Causal mask where the tile reaches past the wave's first position; running
-      // max.  Register r of block kb holds key 32kb + 8(r/4) + 4hl + r%4.
-      if (key0 + 63 > pmin) {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int32_t key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key > rpos) sacc[kb][r] = -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kb][s]),
+                                                            as_bf16x8(qb[s]), sacc[kb], 0, 0, 0);
+    }
+    // Causal mask where the tile reaches past the wave's first position; running
+    // max.  Register r of block kb holds key 32kb + 8(r/4) + 4hl + r%4.
+    if (key0 + 63 > pmin) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m_run, mt * scale_log2);
-      if (__any(mn != m_run)) {  // rescale only when some running max moved
-        const float alpha = exp2f(m_run - mn);
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        m_run = mn;
-      }
-      float psum = 0.f;
-      u32x4 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = exp2f(fmaf(sacc[kb][r], scale_log2, -m_run));
-          psum += p[r];
+          const int32_t key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key > rpos) sacc[kb][r] = -INFINITY;
         }
+    }
+    float mt = -INFINITY;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          pb[kb][s2].x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
-          pb[kb][s2].y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
-          pb[kb][s2].z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
-          pb[kb][s2].w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
-        }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m_run, mt * scale_log2);
+    if (__any(mn != m_run)) {  // rescale only when some running max moved
+      const float alpha = fast_exp2(m_run - mn);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      m_run = mn;
+    }
+    float psum = 0.f;
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_run));
+        psum += p[r];
       }
-      l_run += psum;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        pb[kb][s2].x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
+        pb[kb][s2].y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
+        pb[kb][s2].z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
+        pb[kb][s2].w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
+      }
+    }
+    l_run += psum;
 
-      // O^T += V^T P^T.  MFMA k index 8*hl + j maps to key 32kb + 16s2 + 8(j/4) + 4hl + j%4,
-      // the same keys this lane's P registers 8s2 .. 8s2+7 hold.
+    // O^T += V^T P^T.  MFMA k index 8*hl + j maps to key 32kb + 16s2 + 8(j/4) + 4hl + j%4,
+    // the same keys this lane's P registers 8s2 .. 8s2+7 hold; the two transposing reads
+    // fetch those keys (kbase + 4hl + 0..3 and kbase + 8 + 4hl + 0..3) at dim 32d + col.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int kbase = 32 * kb + 16 * s2 + 4 * hl;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kbase = 32 * kb + 16 * s2;
+        const int r0 = kbase + vkey_in, r1 = r0 + 8;
+        u32x4 a[DB];
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const int dim = 32 * d + col;
-            const uint32_t* vr = Vt[buf] + ((dim * VTS + kbase) >> 1);
-            const u32x2 lo = *(const u32x2*)vr;
-            const u32x2 hi = *(const u32x2*)(vr + 4);
-            const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a),
-                                                             as_bf16x8(pb[kb][s2]), oacc[d],
-                                                             0, 0, 0);
-          }
+        for (int d = 0; d < DB; ++d) {
+          const int dim = 32 * d + vdim_in;
+          const int u = dim >> 3, half = dim & 7;
+          const u32x2 lo = ds_read_tr(Vs[buf] + (r0 * CPR + (u ^ vswz<CPR>(r0))) * 8 + half);
+          const u32x2 hi = ds_read_tr(Vs[buf] + (r1 * CPR + (u ^ vswz<CPR>(r1))) * 8 + half);
+          a[d] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
-    }
-    // Tile t+1 (staged in registers since the last iteration) into the other buffer,
-    // tile t+2 into flight, ids of tile t+3 into flight.
-    if (t + 1 < ntile) {
-      store_stage(buf ^ 1);
-      if (t + 2 < ntile) {
-        issue_loads(t + 2, ids_a);
-        fetch_ids(t + 3, ids_a);
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[d]),
+                                                           as_bf16x8(pb[kb][s2]), oacc[d],
+                                                           0, 0, 0);
       }
-    }
-    __syncthreads();
   }
 
   if (!row_valid) return;
@@ -284,6 +338,7 @@ hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int32_t n = b.n_prefill_items;
   const int32_t grid = ((n + N_XCD - 1) / N_XCD) * N_XCD;
+  static_assert(STAGES - 2 <= 2, "wait_vmcnt cases cover up to two later tiles");
   hipLaunchKernelGGL((prefill_attn_kernel<D>), dim3(grid), dim3(PF_THREADS), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out,
                      (const int4*)b.prefill_work, n, b.cu_seqlens, b.seen, b.block_offsets,

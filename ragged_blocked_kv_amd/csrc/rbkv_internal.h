@@ -12,8 +12,8 @@ namespace rbkv {
 
 // Keys per decode tile: one key per lane of a 64-wide wavefront.
 constexpr int KT = 64;
-// Query rows (tokens x heads of one kv group) per prefill workgroup: 4 waves x 32.
-constexpr int PF_ROWS = 128;
+// Query rows (tokens x heads of one kv group) per prefill workgroup: 8 waves x 32.
+constexpr int PF_ROWS = 256;
 constexpr int MAX_GROUP = 16;
 constexpr int MAX_SEQS_LIMIT = 2048;
 constexpr int MAX_TOKENS_LIMIT = 1 << 20;
