@@ -37,6 +37,9 @@ COMMON_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Every value on this path is finite (masking uses -inf, which stays honoured), so
+    # max/min need no NaN canonicalisation and fuse with DPP lane moves.
+    "-fno-honor-nans",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

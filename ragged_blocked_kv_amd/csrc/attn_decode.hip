@@ -89,8 +89,16 @@ __device__ __forceinline__ u32x4 pack_chunk<float>(const float* f) {
   return r;
 }
 
-template <typename T, int D, int GMAX>
-__global__ __launch_bounds__(64) void decode_attn_kernel(
+// Waves per SIMD the kernel is compiled for: two where the registers allow it (tile data
+// in flight is what hides HBM latency), one otherwise.
+template <typename T, int GMAX>
+constexpr int dec_waves_per_simd() { return (sizeof(T) == 4 || GMAX >= 16) ? 1 : 2; }
+
+// ONE_BLK: blocks hold at least 64 keys, so every 64-key tile lies inside one block.
+template <typename T, int D, int GMAX, bool ONE_BLK>
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(dec_waves_per_simd<T, GMAX>(), dec_waves_per_simd<T, GMAX>())))
+void decode_attn_kernel(
     const T* __restrict__ qkv, const T* __restrict__ pool, T* __restrict__ out,
     float* __restrict__ ws, const int4* __restrict__ work, const int32_t* __restrict__ tok2seq,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ block_off,
@@ -98,9 +106,10 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
     int32_t split_tiles, float scale_log2) {
   using Gm = DecGeom<T, D>;
   constexpr int CPR = Gm::CPR, KPI = Gm::KPI, NI = Gm::NI, VW = Gm::VW;
+  constexpr int MAXNB = 4;  // blocks a 64-key tile can span (block size 16)
   __shared__ u32x4 ktile[64 * CPR];
   __shared__ u32x4 qs[GMAX * CPR];
-  __shared__ float ps[64 * GMAX];
+  __shared__ __attribute__((aligned(16))) float ps[64 * GMAX];
 
   const int lane = threadIdx.x;
   const int4 w = work[blockIdx.x];
@@ -112,13 +121,19 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
   const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
   const int32_t key_end = min(nkeys, t_end * 64);
   const int32_t* bids = block_ids + block_off[seq];
+  const int bsh = 31 - __builtin_clz(bs);             // block sizes are powers of two
+  const int32_t last_blk = (key_end - 1) >> bsh;
   const size_t head_stride = (size_t)bs * D;          // one (block, kv, head) slab
+  const size_t blk_stride = (size_t)2 * Hkv * head_stride;
   const size_t v_off = (size_t)Hkv * head_stride;     // keys -> values of the same block
-
-  // Query rows of the group's G heads into LDS.
-  const int32_t row_elems = (Hq + 2 * Hkv) * D;
-  const T* qrow = qkv + (size_t)token * row_elems + (size_t)kvh * G * D;
-  for (int u = lane; u < G * CPR; u += 64) qs[u] = ld16(qrow + (size_t)(u / CPR) * D + (u % CPR) * VW);
+  const T* pool_g = pool + (size_t)kvh * head_stride;
+  // Query rows of the group into LDS (read back as broadcasts); heads past G (padding up
+  // to GMAX) repeat the last real head, so the head loops need no branches.
+  {
+    const T* qrow = qkv + (size_t)token * (Hq + 2 * Hkv) * D + (size_t)kvh * G * D;
+    for (int u = lane; u < GMAX * CPR; u += 64)
+      qs[u] = ld16(qrow + (size_t)min(u / CPR, G - 1) * D + (u % CPR) * VW);
+  }
 
   float m[GMAX], lsum[GMAX], o[GMAX][VW];
 #pragma unroll
@@ -130,29 +145,52 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
   }
   const int cl = lane % CPR;  // chunk column this lane loads / accumulates
   const int kg = lane / CPR;  // key sub-row within a load instruction
+  const int lane_off = kg * D + cl * VW;  // element offset of this lane inside a row group
+
+  // Block ids of a tile are uniform: they come through the scalar cache, a tile ahead.
+  auto fetch_ids = [&](int32_t tt, int32_t* ids) {
+    const int32_t b0 = min((tt * 64) >> bsh, last_blk);
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j) ids[j] = bids[min(b0 + j, last_blk)];
+  };
+  // Uniform base of row group i of a tile: keys key0 + i*KPI .. +KPI-1 share one block
+  // (KPI <= 8 <= bs).  A group wholly past key_end re-reads the tile's first group.
+  auto row_base = [&](int32_t tt, const int32_t* ids, int i) -> const T* {
+    const int32_t key0 = tt * 64;
+    if constexpr (ONE_BLK)  // the tile lies in one block: fixed row offsets from one base
+      return pool_g + (size_t)ids[0] * blk_stride + (size_t)(key0 & (bs - 1)) * D +
+             (size_t)(i * KPI) * D;
+    int32_t k = key0 + i * KPI;
+    k = k < key_end ? k : key0;
+    const int jb = (k >> bsh) - (key0 >> bsh);
+    const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
+    return pool_g + (size_t)id * blk_stride + (size_t)(k & (bs - 1)) * D;
+  };
+
+  u32x4 kr[NI], vr[NI];
+  int32_t ids_cur[MAXNB], ids_next[MAXNB];
+  fetch_ids(t_begin, ids_cur);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const T* rb = row_base(t_begin, ids_cur, i);
+    kr[i] = ld16(rb + lane_off);
+    vr[i] = ld16((rb + v_off) + lane_off);
+  }
+  fetch_ids(min(t_begin + 1, t_end - 1), ids_next);
 
   for (int32_t tt = t_begin; tt < t_end; ++tt) {
-    const int32_t key0 = tt * 64;
-    u32x4 kreg[NI], vreg[NI];
+    // The next tile is always prefetched (the last tile re-reads itself, an L2 hit), so
+    // the loads need no branches and the V registers are refilled in place.
+    const int32_t tn = min(tt + 1, t_end - 1);
+    __syncthreads();  // previous tile's readers of ktile / ps are done
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int32_t key = key0 + i * KPI + kg;
-      kreg[i] = u32x4{0, 0, 0, 0};
-      vreg[i] = u32x4{0, 0, 0, 0};
-      if (key < key_end) {
-        const int64_t blk = bids[key / bs];
-        const T* src = pool + (size_t)(blk * 2 * Hkv + kvh) * head_stride +
-                       (size_t)(key % bs) * D + cl * VW;
-        kreg[i] = ld16(src);
-        vreg[i] = ld16(src + v_off);
-      }
-    }
-    __syncthreads();  // previous tile's LDS readers are done
-#pragma unroll
-    for (int i = 0; i < NI; ++i) ktile[kslot<CPR>(i * KPI + kg, cl)] = kreg[i];
+    for (int i = 0; i < NI; ++i) ktile[kslot<CPR>(i * KPI + kg, cl)] = kr[i];
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = ld16(row_base(tn, ids_next, i) + lane_off);
 
-    // Scores: lane = key.
+    // Scores: lane = key; every padding head repeats a real one, so no branches.
+    const int32_t key0 = tt * 64;
     float s[GMAX];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) s[h] = 0.f;
@@ -160,58 +198,64 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
     for (int c = 0; c < CPR; ++c) {
       const u32x4 kc = ktile[kslot<CPR>(lane, c)];
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h)
-        if (h < G) s[h] = dot_chunk(qs[h * CPR + c], kc, s[h], T{});
+      for (int h = 0; h < GMAX; ++h) s[h] = dot_chunk(qs[h * CPR + c], kc, s[h], T{});
     }
     const bool valid = key0 + lane < key_end;
     float alpha[GMAX];
+    float pe[GMAX];
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
-      if (h < G) {
-        const float sc = valid ? s[h] * scale_log2 : -INFINITY;
-        const float mn = fmaxf(m[h], wave_max(sc));
-        alpha[h] = exp2f(m[h] - mn);
-        m[h] = mn;
-        const float pe = exp2f(sc - mn);
-        lsum[h] = lsum[h] * alpha[h] + pe;
-        ps[lane * GMAX + h] = pe;
-      }
+      const float sc = valid ? s[h] * scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[h], wave_max_dpp(sc));
+      alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
+      m[h] = mn;
+      pe[h] = __builtin_amdgcn_exp2f(sc - mn);
+      lsum[h] = lsum[h] * alpha[h] + pe[h];
+    }
+#pragma unroll
+    for (int h = 0; h < GMAX; h += (GMAX >= 4 ? 4 : GMAX)) {
+      if constexpr (GMAX >= 4)
+        *(f32x4*)(ps + lane * GMAX + h) = f32x4{pe[h], pe[h + 1], pe[h + 2], pe[h + 3]};
+      else
+#pragma unroll
+        for (int j = 0; j < GMAX; ++j) ps[lane * GMAX + j] = pe[j];
     }
     __syncthreads();
 
-    // P.V: lane accumulates VW columns over keys i*KPI + kg.
+    // P.V: lane accumulates VW columns over keys i*KPI + kg; each V register is
+    // refilled with the next tile's row as soon as it has been used.
 #pragma unroll
     for (int h = 0; h < GMAX; ++h)
-      if (h < G) {
 #pragma unroll
-        for (int e = 0; e < VW; ++e) o[h][e] *= alpha[h];
-      }
+      for (int e = 0; e < VW; ++e) o[h][e] *= alpha[h];
+    const bool partial = key0 + 64 > key_end;  // keys past the end: zero their values
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float v[VW];
-      unpack_chunk<T>(vreg[i], v);
+      u32x4 vi = vr[i];
+      if (partial && key0 + i * KPI + kg >= key_end) vi = u32x4{0, 0, 0, 0};
+      unpack_chunk<T>(vi, v);
+      vr[i] = ld16((row_base(tn, ids_next, i) + v_off) + lane_off);
       const float* pk = ps + (i * KPI + kg) * GMAX;
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h)
-        if (h < G) {
-          const float ph = pk[h];
+      for (int h = 0; h < GMAX; ++h) {
+        const float ph = pk[h];
 #pragma unroll
-          for (int e = 0; e < VW; ++e) o[h][e] = fmaf(ph, v[e], o[h][e]);
-        }
+        for (int e = 0; e < VW; ++e) o[h][e] = fmaf(ph, v[e], o[h][e]);
+      }
     }
+    fetch_ids(min(tt + 2, t_end - 1), ids_next);
   }
 
   // Reduce over the lanes that share a chunk column, and the row sums over all lanes.
 #pragma unroll
   for (int h = 0; h < GMAX; ++h) {
-    if (h < G) {
 #pragma unroll
-      for (int e = 0; e < VW; ++e) {
+    for (int e = 0; e < VW; ++e) {
 #pragma unroll
-        for (int off = CPR; off < 64; off <<= 1) o[h][e] += __shfl_xor(o[h][e], off, 64);
-      }
-      lsum[h] = wave_sum(lsum[h]);
+      for (int off = CPR; off < 64; off <<= 1) o[h][e] += __shfl_xor(o[h][e], off, 64);
     }
+    lsum[h] = wave_sum_dpp(lsum[h]);
   }
   if (slot < 0) {
     if (lane < CPR) {
@@ -228,10 +272,12 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(
   } else {
     float* part = ws + (size_t)slot * G * (D + 2);
     if (lane == 0) {
-      for (int h = 0; h < G; ++h) {
-        part[h] = m[h];
-        part[G + h] = lsum[h];
-      }
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+        if (h < G) {
+          part[h] = m[h];
+          part[G + h] = lsum[h];
+        }
     }
     if (lane < CPR) {
 #pragma unroll
@@ -250,11 +296,18 @@ hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
                     void* out, float* ws, hipStream_t stream) {
   const int G = s.n_q_heads / s.n_kv_heads;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((decode_attn_kernel<T, D, GMAX>), dim3(b.n_decode_items), dim3(64), 0,
-                     stream, (const T*)qkv, (const T*)pool, (T*)out, ws,
-                     (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
-                     b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
-                     scale_log2);
+  if (s.block_size >= 64)
+    hipLaunchKernelGGL((decode_attn_kernel<T, D, GMAX, true>), dim3(b.n_decode_items), dim3(64),
+                       0, stream, (const T*)qkv, (const T*)pool, (T*)out, ws,
+                       (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
+                       b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
+                       scale_log2);
+  else
+    hipLaunchKernelGGL((decode_attn_kernel<T, D, GMAX, false>), dim3(b.n_decode_items),
+                       dim3(64), 0, stream, (const T*)qkv, (const T*)pool, (T*)out, ws,
+                       (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
+                       b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
+                       scale_log2);
   return hipGetLastError();
 }
 
