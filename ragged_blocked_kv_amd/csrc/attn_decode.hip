@@ -203,10 +203,12 @@ void decode_attn_kernel(
     const bool valid = key0 + lane < key_end;
     float alpha[GMAX];
     float pe[GMAX];
+    bool any_moved = false;  // uniform: some running max changed this tile
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       const float sc = valid ? s[h] * scale_log2 : -INFINITY;
       const float mn = fmaxf(m[h], wave_max_dpp(sc));
+      any_moved |= mn != m[h];
       alpha[h] = __builtin_amdgcn_exp2f(m[h] - mn);
       m[h] = mn;
       pe[h] = __builtin_amdgcn_exp2f(sc - mn);
@@ -224,24 +226,56 @@ void decode_attn_kernel(
 
     // P.V: lane accumulates VW columns over keys i*KPI + kg; each V register is
     // refilled with the next tile's row as soon as it has been used.
+    if (any_moved) {
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h)
+      for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-      for (int e = 0; e < VW; ++e) o[h][e] *= alpha[h];
+        for (int e = 0; e < VW; ++e) o[h][e] *= alpha[h];
+    }
     const bool partial = key0 + 64 > key_end;  // keys past the end: zero their values
+    if constexpr (sizeof(T) == 2 && GMAX <= 4) {
+      // bf16, up to 4 heads: two keys per v_dot2_f32_bf16 (measured faster than fp32 FMAs
+      // there; with 8+ heads the extra registers cost more than the saved issue slots).  Rows i and i+1 (keys k and k + KPI) are
+      // interleaved per column with v_perm_b32 and their weights packed to a bf16 pair.
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float v[VW];
-      u32x4 vi = vr[i];
-      if (partial && key0 + i * KPI + kg >= key_end) vi = u32x4{0, 0, 0, 0};
-      unpack_chunk<T>(vi, v);
-      vr[i] = ld16((row_base(tn, ids_next, i) + v_off) + lane_off);
-      const float* pk = ps + (i * KPI + kg) * GMAX;
+      for (int i = 0; i < NI; i += 2) {
+        u32x4 a = vr[i], b = vr[i + 1];
+        if (partial && key0 + i * KPI + kg >= key_end) a = u32x4{0, 0, 0, 0};
+        if (partial && key0 + (i + 1) * KPI + kg >= key_end) b = u32x4{0, 0, 0, 0};
+        vr[i] = ld16((row_base(tn, ids_next, i) + v_off) + lane_off);
+        vr[i + 1] = ld16((row_base(tn, ids_next, i + 1) + v_off) + lane_off);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+        uint32_t vp[8];
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        const float ph = pk[h];
+        for (int j = 0; j < 4; ++j) {
+          vp[2 * j] = __builtin_amdgcn_perm(bw[j], aw[j], 0x05040100u);
+          vp[2 * j + 1] = __builtin_amdgcn_perm(bw[j], aw[j], 0x07060302u);
+        }
+        const float* pa = ps + (i * KPI + kg) * GMAX;
+        const float* pb = ps + ((i + 1) * KPI + kg) * GMAX;
 #pragma unroll
-        for (int e = 0; e < VW; ++e) o[h][e] = fmaf(ph, v[e], o[h][e]);
+        for (int h = 0; h < GMAX; ++h) {
+          const bf16x2v pp = as_bf16x2(pack_bf16x2(pa[h], pb[h]));
+#pragma unroll
+          for (int e = 0; e < VW; ++e)
+            o[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, as_bf16x2(vp[e]), o[h][e], false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float v[VW];
+        u32x4 vi = vr[i];
+        if (partial && key0 + i * KPI + kg >= key_end) vi = u32x4{0, 0, 0, 0};
+        unpack_chunk<T>(vi, v);
+        vr[i] = ld16((row_base(tn, ids_next, i) + v_off) + lane_off);
+        const float* pk = ps + (i * KPI + kg) * GMAX;
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          const float ph = pk[h];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) o[h][e] = fmaf(ph, v[e], o[h][e]);
+        }
       }
     }
     fetch_ids(min(tt + 2, t_end - 1), ids_next);

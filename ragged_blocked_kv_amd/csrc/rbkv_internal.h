@@ -19,8 +19,8 @@ constexpr int MAX_SEQS_LIMIT = 2048;
 constexpr int MAX_TOKENS_LIMIT = 1 << 20;
 constexpr int MAX_BLOCKS_LIMIT = 1 << 26;
 // Decode split-K sizing: aim for about this many decode work items per batch.
-constexpr int64_t DECODE_TARGET_ITEMS = 16384;
-constexpr int MIN_SPLIT_TILES = 2;
+constexpr int64_t DECODE_TARGET_ITEMS = 6144;
+constexpr int MIN_SPLIT_TILES = 4;
 constexpr int MAX_SPLIT_TILES = 64;
 
 // Header of the staged batch (int32 words at the start of the staging area).
