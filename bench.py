@@ -48,7 +48,7 @@ def algorithmic_work(wl):
         "prefill_flops": float(4 * d * Hq * (n[chunk] * s[chunk] +
                                              n[chunk] * (n[chunk] + 1) // 2).sum()),
         "attention_bytes": float(e * (2 * Hkv * d * L.sum() + 2 * Hq * d * n.sum())),
-        "append_bytes": float(e * d * n.sum() * (2 * (Hq + Hkv) + 2 * Hkv + Hkv)),
+        "append_bytes": float(2 * e * d * n.sum() * (Hq + 2 * Hkv)),
     }
 
 
@@ -69,7 +69,65 @@ def measured_traffic(kernel_file, workload):
         return None
     if not rec or rec.get("source_sha") != kernel_source_digest(kernel_file):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_launch")  # bytes per launch (fetch + write), scaled
+
+
+KERNEL_FILES = {"prefill_attn_kernel": "attn_prefill.hip", "decode_attn_kernel": "attn_decode.hip",
+                "append_rotary_kernel": "append_rotary.hip", "combine_kernel": "attn_combine.hip",
+                "meta_build_kernel": "meta_build.hip"}
+
+
+def copy_calibration(nbytes, reps):
+    """A plain device-to-device copy of a known size, for scaling the HBM counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def _counter_per_dispatch(csv_path, counter, name_filter):
+    import csv as _csv
+    import collections
+
+    per = collections.defaultdict(float)
+    for row in _csv.DictReader(open(csv_path)):
+        if row["Counter_Name"] == counter and name_filter(row["Kernel_Name"]):
+            per[row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return per
+
+
+def traffic_from_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_bytes,
+                          workload, out_path):
+    """Reduce rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) to HBM bytes per
+    launch of each library kernel, scaled by what the same counters read for a copy of
+    cal_bytes bytes (which reads and writes exactly cal_bytes)."""
+    is_copy = lambda n: "rbkv" not in n
+    cf = _counter_per_dispatch(cal_fetch_csv, "FETCH_SIZE", is_copy)
+    cw = _counter_per_dispatch(cal_write_csv, "WRITE_SIZE", is_copy)
+    big = lambda d: max(d.values())  # the calibration copy is the largest dispatch
+    f_scale = cal_bytes / (big(cf) * 1024.0)
+    w_scale = cal_bytes / (big(cw) * 1024.0)
+    rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    for kname, kfile in KERNEL_FILES.items():
+        sel = lambda n, k=kname: k in n
+        fv = list(_counter_per_dispatch(fetch_csv, "FETCH_SIZE", sel).values())
+        wv = list(_counter_per_dispatch(write_csv, "WRITE_SIZE", sel).values())
+        if not fv or not wv:
+            continue
+        fb = float(np.mean(fv)) * 1024.0 * f_scale
+        wb = float(np.mean(wv)) * 1024.0 * w_scale
+        rec[f"{kfile}:{workload}"] = {
+            "source_sha": kernel_source_digest(kfile),
+            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+            "bytes_per_launch": fb + wb, "dispatches": len(fv),
+            "fetch_scale": f_scale, "write_scale": w_scale,
+        }
+    json.dump(rec, open(out_path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(wl, qkv_cpu, hist_fn, budget_s):
@@ -129,7 +187,21 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a device copy of BYTES (HBM counter calibration)")
+    ap.add_argument("--traffic-from", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV",
+                             "CAL_BYTES"),
+                    help="reduce rocprofv3 counter CSVs into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        f, w, cf, cw, cb = args.traffic_from
+        traffic_from_counters(f, w, cf, cw, int(cb), args.workload,
+                              os.path.join(ROOT, "profiles", "traffic.json"))
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 3)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(shard by heads or by sequences and run one process per GPU instead)",
