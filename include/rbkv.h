@@ -110,7 +110,8 @@ typedef struct rbkv_shape {
  *   token_to_seq[T]     owning sequence of each packed token
  *   pos[T]              absolute position of each packed token
  *   decode_work, prefill_work, combine_work: work-item records (4 int32 each) of the
- *                       three attention kernels; their format is internal. */
+ *                       three attention kernels; their format is internal (prefill_work
+ *                       holds one record per chunk sequence, longest first). */
 typedef struct rbkv_batch {
   rbkv_shape shape; /* the shape this batch was built for */
   int32_t S;
@@ -121,6 +122,8 @@ typedef struct rbkv_batch {
   int32_t n_prefill_items;
   int32_t n_partials;    /* split-K partial-result slots needed in the workspace */
   int32_t n_combine_items;
+  int32_t n_prefill_seqs;      /* sequences whose chunk runs on the matrix cores */
+  int32_t prefill_qtiles_max;  /* most query tiles of one such sequence */
   const int32_t* cu_seqlens;
   const int32_t* seen;
   const int32_t* kv_len;

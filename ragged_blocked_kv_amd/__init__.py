@@ -69,7 +69,8 @@ _P = ctypes.POINTER(ctypes.c_int32)
 class Batch(ctypes.Structure):
     _fields_ = [("shape", Shape)] + [(n, ctypes.c_int32) for n in (
         "S", "T", "n_blocks_used", "split_tiles", "n_decode_items", "n_prefill_items",
-        "n_partials", "n_combine_items")] + [(n, ctypes.c_void_p) for n in (
+        "n_partials", "n_combine_items", "n_prefill_seqs", "prefill_qtiles_max")] + [
+        (n, ctypes.c_void_p) for n in (
         "cu_seqlens", "seen", "kv_len", "block_offsets", "block_ids", "token_to_seq", "pos",
         "decode_work", "prefill_work", "combine_work")]
 

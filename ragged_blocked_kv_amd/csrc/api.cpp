@@ -2,6 +2,7 @@
 // Every check runs before any HIP call, so each error path is testable without a GPU.
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "rbkv_internal.h"
@@ -187,12 +188,17 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
 
   const int32_t split = choose_split_tiles(dec_tiles);
   int64_t ndec = 0, npre = 0, npart = 0, ncomb = 0;
+  int32_t npseq = 0, nqt_max = 0;
   for (int32_t i = 0; i < S; ++i) {
     SeqPlan p = plan_sequence(n_new[i], seen[i], Hkv, split, mfma, qtt);
     ndec += p.dec_items;
     npre += p.pre_items;
     npart += p.partials;
     ncomb += p.comb_items;
+    if (p.pre_items > 0) {
+      ++npseq;
+      nqt_max = std::max(nqt_max, (int32_t)cdiv64(n_new[i], qtt));
+    }
   }
   const Caps caps = work_caps(s);  // bounds every valid batch; checked to fail loudly
   if (ndec > caps.dec || npre > caps.pre || ncomb > caps.comb || npart > caps.dec ||
@@ -211,6 +217,8 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
   b.n_prefill_items = (int32_t)npre;
   b.n_partials = (int32_t)npart;
   b.n_combine_items = (int32_t)ncomb;
+  b.n_prefill_seqs = npseq;
+  b.prefill_qtiles_max = nqt_max;
   b.cu_seqlens = (const int32_t*)(dm + L.cu);
   b.seen = (const int32_t*)(dm + L.seen);
   b.kv_len = (const int32_t*)(dm + L.kv_len);
@@ -244,6 +252,7 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
   hp[H_NPRE] = (int32_t)npre;
   hp[H_NPART] = (int32_t)npart;
   hp[H_NCOMB] = (int32_t)ncomb;
+  hp[H_NPSEQ] = npseq;
   int32_t* hn = (int32_t*)((char*)host_pinned + L.n_new);
   int32_t* hs = (int32_t*)((char*)host_pinned + L.seen);
   int32_t* hb = (int32_t*)((char*)host_pinned + L.block_ids);

@@ -81,8 +81,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int D>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
-    uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_items,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
+    uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_groups, int32_t nq_max,
+    int32_t qtt, const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
     int32_t Hkv, int32_t G, int32_t bs, float scale_log2) {
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
@@ -96,19 +96,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[STAGES][64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[STAGES][64 * D];
 
-  // XCD-aware mapping: block b runs on XCD b % 8; give each XCD a contiguous run of
-  // items so that the query tiles of one (sequence, kv head) share an L2.
-  const int32_t per_xcd = (n_items + N_XCD - 1) / N_XCD;
-  const int32_t item = (int32_t)(blockIdx.x % N_XCD) * per_xcd + (int32_t)(blockIdx.x / N_XCD);
-  if (item >= n_items) return;  // whole workgroup leaves together
+  // Work placement.  Block b runs on XCD b % 8.  The (sequence, kv head) groups, in the
+  // order of the ranked chunk sequences (longest first), are dealt round-robin over the
+  // XCDs, so each XCD gets an even share; the query tiles of one group run back to back
+  // on one XCD (longest tile first) and share its L2.  Slots past a group's tiles exit.
+  const int32_t xcd = (int32_t)(blockIdx.x % N_XCD);
+  const int32_t k = (int32_t)(blockIdx.x / N_XCD);
+  const int32_t gidx = (k / nq_max) * N_XCD + xcd;
+  if (gidx >= n_groups) return;  // whole workgroup leaves together
+  const int4 rec = work[gidx / Hkv];
+  const int32_t seq = rec.x, nqt = rec.y;
+  const int32_t jq = k % nq_max;
+  if (jq >= nqt) return;
+  const int32_t kvh = gidx % Hkv;
+  const int32_t qt = nqt - 1 - jq;
+  const int32_t q0 = qt * qtt;
+  const int32_t q1 = min(cu[seq + 1] - cu[seq], q0 + qtt);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hl = lane >> 5;     // half of the wave
   const int col = lane & 31;    // query row within the wave's 32
 
-  const int4 w = work[item];
-  const int32_t seq = w.x, kvh = w.y, q0 = w.z, q1 = w.w;
   const int32_t n_tok = q1 - q0;
   const int32_t rows = n_tok * G;
   const int32_t seen = seen_arr[seq];
@@ -236,12 +245,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
       }
+      __builtin_amdgcn_s_setprio(1);  // let the other wave's softmax fill the MFMA shadow
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kb][s]),
                                                             as_bf16x8(qb[s]), sacc[kb], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
     // Causal mask where the tile reaches past the wave's first position; running
     // max.  Register r of block kb holds key 32kb + 8(r/4) + 4hl + r%4.
@@ -308,11 +319,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
           const u32x2 hi = ds_read_tr(Vs[buf] + (r1 * CPR + (u ^ vswz<CPR>(r1))) * 8 + half);
           a[d] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int d = 0; d < DB; ++d)
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[d]),
                                                            as_bf16x8(pb[kb][s2]), oacc[d],
                                                            0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
       }
   }
 
@@ -336,12 +349,14 @@ template <int D>
 hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
                     void* out, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  const int32_t n = b.n_prefill_items;
-  const int32_t grid = ((n + N_XCD - 1) / N_XCD) * N_XCD;
+  const int32_t n_groups = b.n_prefill_seqs * s.n_kv_heads;
+  const int32_t grid = ((n_groups + N_XCD - 1) / N_XCD) * b.prefill_qtiles_max * N_XCD;
+  const int32_t qtt = q_tile_tokens(s.n_q_heads / s.n_kv_heads);
   static_assert(STAGES - 2 <= 2, "wait_vmcnt cases cover up to two later tiles");
   hipLaunchKernelGGL((prefill_attn_kernel<D>), dim3(grid), dim3(PF_THREADS), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out,
-                     (const int4*)b.prefill_work, n, b.cu_seqlens, b.seen, b.block_offsets,
+                     (const int4*)b.prefill_work, n_groups, b.prefill_qtiles_max, qtt,
+                     b.cu_seqlens, b.seen, b.block_offsets,
                      b.block_ids, s.n_q_heads, s.n_kv_heads, s.n_q_heads / s.n_kv_heads,
                      s.block_size, scale_log2);
   return hipGetLastError();

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
   __shared__ int32_t offs[N_SCANS][MAX_SEQS_LIMIT + 1];
   __shared__ int32_t s_seen[MAX_SEQS_LIMIT];
   __shared__ int32_t s_nsplit[MAX_SEQS_LIMIT];
+  __shared__ long long s_pwork[MAX_SEQS_LIMIT];  // chunk work proxy, -1 if not a chunk
 
   const int tid = threadIdx.x;
   const int32_t S = staging[H_S];
@@ -62,7 +63,6 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
   const bool mfma = staging[H_MFMA] != 0;
   const int32_t qtt = staging[H_QTT];
   const int32_t n_dec = staging[H_NDEC];
-  const int32_t n_pre = staging[H_NPRE];
   const int32_t n_comb = staging[H_NCOMB];
   const int32_t* n_new = staging + HDR_INTS;
   const int32_t* seen = n_new + max_seqs;
@@ -78,6 +78,7 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
     vals[5][i] = p.comb_items;
     s_seen[i] = s;
     s_nsplit[i] = p.nsplit;
+    s_pwork[i] = p.pre_items > 0 ? (long long)prefill_work_proxy(n, s, qtt) : -1;
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
@@ -120,18 +121,22 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
     }
     dec[w] = r;
   }
-  for (int w = tid; w < n_pre; w += MB_THREADS) {
-    const int i = upper_index(s_pre, S, w);
-    const int32_t local = w - s_pre[i];
-    const int32_t n = vals[0][i];
-    const int32_t nqt = (int32_t)cdiv64(n, qtt);
-    const int32_t qt = nqt - 1 - local % nqt;  // last (longest) query tile first
+  // Chunk sequences ranked by work, longest first (ties by batch order): the prefill
+  // kernel deals their (sequence, kv head) groups round-robin over the XCDs.
+  for (int i = tid; i < S; i += MB_THREADS) {
+    const long long wi = s_pwork[i];
+    if (wi < 0) continue;
+    int32_t rank = 0;
+    for (int j = 0; j < S; ++j) {
+      const long long wj = s_pwork[j];
+      rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
+    }
     int4 r;
     r.x = i;
-    r.y = local / nqt;
-    r.z = qt * qtt;
-    r.w = min(n, (qt + 1) * qtt);
-    pre[w] = r;
+    r.y = (int32_t)cdiv64(vals[0][i], qtt);
+    r.z = 0;
+    r.w = 0;
+    pre[rank] = r;
   }
   for (int w = tid; w < n_comb; w += MB_THREADS) {
     const int i = upper_index(s_comb, S, w);

@@ -26,7 +26,7 @@ constexpr int MAX_SPLIT_TILES = 64;
 // Header of the staged batch (int32 words at the start of the staging area).
 enum HeaderWord {
   H_S = 0, H_T, H_NBLK, H_SPLIT, H_HKV, H_MFMA, H_QTT, H_NDEC, H_NPRE, H_NPART, H_NCOMB,
-  HDR_INTS = 16
+  H_NPSEQ, HDR_INTS = 16
 };
 
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -67,6 +67,12 @@ __host__ __device__ inline SeqPlan plan_sequence(int32_t n, int32_t seen, int32_
     p.dec_items = Hkv * n;
   }
   return p;
+}
+
+// Work proxy used to order chunk sequences longest first on the matrix cores: query
+// tiles times the keys an average tile sees (monotone in the 64-key tiles it streams).
+__host__ __device__ inline int64_t prefill_work_proxy(int32_t n, int32_t seen, int32_t qtt) {
+  return cdiv64(n, qtt) * (2 * (int64_t)seen + n);
 }
 
 // Capacities of the work lists for a shape (upper bounds over every valid batch).

@@ -103,6 +103,6 @@ class Engine:
             "token_to_seq": arr(b.token_to_seq, T),
             "pos": arr(b.pos, T),
             "decode_work": arr(b.decode_work, 4 * b.n_decode_items).reshape(-1, 4),
-            "prefill_work": arr(b.prefill_work, 4 * b.n_prefill_items).reshape(-1, 4),
+            "prefill_work": arr(b.prefill_work, 4 * b.n_prefill_seqs).reshape(-1, 4),
             "combine_work": arr(b.combine_work, 4 * b.n_combine_items).reshape(-1, 4),
         }

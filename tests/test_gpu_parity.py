@@ -73,10 +73,18 @@ def check_work_coverage(md, b, wl):
             assert t0 < tiles
         cover.setdefault((tok, kvh), []).append(rng)
     cu = md["cu_seqlens"]
-    for seq, kvh, q0, q1 in md["prefill_work"]:
-        assert 0 <= q0 < q1 <= cu[seq + 1] - cu[seq]
-        for tok in range(cu[seq] + q0, cu[seq] + q1):
-            cover.setdefault((tok, kvh), []).append((0, pos[tok] + 1))
+    # one record per chunk sequence, ranked by work (longest first); the prefill kernel
+    # covers all its query tiles for every kv head
+    ranked = [int(r[0]) for r in md["prefill_work"]]
+    assert len(set(ranked)) == len(ranked) == b.n_prefill_seqs
+    work = [(-(-int(wl.n_new[i]) // max(1, 256 // (wl.n_q_heads // Hkv)))) *
+            (2 * int(wl.seen[i]) + int(wl.n_new[i])) for i in ranked]
+    assert all(a >= c for a, c in zip(work, work[1:]))
+    for seq, nqt, _, _ in md["prefill_work"]:
+        assert nqt >= 1
+        for kvh in range(Hkv):
+            for tok in range(cu[seq], cu[seq + 1]):
+                cover.setdefault((tok, kvh), []).append((0, pos[tok] + 1))
     assert len(cover) == T * Hkv
     for (tok, kvh), rs in cover.items():
         rs = sorted(rs)
