@@ -58,12 +58,25 @@ __device__ __forceinline__ bf16x8v as_bf16x8(u32x4 v) { return __builtin_bit_cas
 // softmax weights under 2^-126 of the running maximum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// HBM -> LDS without registers: lane l writes its 16 bytes at dst + 16*l (dst must be
-// wave-uniform).  Kept in a device function: used directly in a kernel template, the
-// builtin makes the host pass drop that kernel's launch stub.
-__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
+
+// HBM -> LDS without registers (global_load_lds_dwordx4): lane l writes its 16 bytes at
+// LDS byte address m0 + 16*l, m0 = lds (wave-uniform).  Written as inline assembly so the
+// compiler does not track the LDS write: it cannot tell the ring stages apart and would
+// otherwise wait for every load in flight before each LDS read, which serialises the
+// tile pipeline.  The kernel orders these writes against its reads itself (explicit
+// vmcnt waits, then a workgroup barrier).  The compiler writes m0 for the operand; one
+// wait state separates that write from the load that uses it.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Max / sum of a value and its copy 32 lanes away (one v_permlane32_swap, no LDS).
+__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+__device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
 __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
@@ -143,13 +156,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   const int32_t pmin = seen + q0 + (wave_active ? w_lo / G : 0);
   const int32_t pmax = seen + q0 + (wave_active ? w_hi / G : 0);
 
-  // Q^T operand: k-step s holds dims 16s + 8*hl .. +8 of this lane's row.
-  u32x4 qb[KSTEPS];
-  {
-    const uint16_t* qr = qkv + ((size_t)(tok0 + rtok) * (Hq + 2 * Hkv) + rhead) * D;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qb[s] = ld16(qr + 16 * s + 8 * hl);
-  }
 
   // Loader role: direct load i of this thread fills LDS chunk i*PF_THREADS + tid of a
   // tile, which holds row (i*PF_THREADS + tid) / CPR and, after the swizzle, a chunk of
@@ -170,15 +176,22 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     for (int j = 0; j < MAXNB; ++j) ids[j] = bids[min(b0 + j, last_blk)];
   };
   const size_t blk_stride = (size_t)2 * Hkv * head_stride;  // elements per pool block
+  // LDS byte address where this wave's first direct load of a K tile lands (stage 0); a
+  // V tile's sits STAGES tiles further.  Stage buf adds buf * TILE_BYTES, load i adds
+  // i * PF_THREADS * 16.
+  constexpr uint32_t TILE_BYTES = 64 * D * 2;
+  const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[0][0]) + wave * 64 * 16);
+  const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[0][0]) + wave * 64 * 16);
   auto issue_loads = [&](int32_t t, const int32_t* ids, int buf) {
+    const uint32_t kd = k_dst0 + buf * TILE_BYTES, vd = v_dst0 + buf * TILE_BYTES;
     if (bs >= 64 && t * 64 + 63 < n_keys) {
       // The whole tile sits in one block: one uniform base, fixed per-thread offsets.
       const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)((t * 64) % bs) * D;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const uint16_t* src = base + krow[i] * D;
-        load_lds16(src + kchk[i] * 8, Ks[buf] + (i * PF_THREADS + wave * 64) * 8);
-        load_lds16(src + v_off + vchk[i] * 8, Vs[buf] + (i * PF_THREADS + wave * 64) * 8);
+        load_lds16(src + kchk[i] * 8, kd + i * PF_THREADS * 16);
+        load_lds16(src + v_off + vchk[i] * 8, vd + i * PF_THREADS * 16);
       }
       return;
     }
@@ -189,11 +202,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
       const int jb = key / bs - b0;
       const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
       const uint16_t* src = pool_g + (size_t)id * blk_stride + (size_t)(key % bs) * D;
-      load_lds16(src + kchk[i] * 8, Ks[buf] + (i * PF_THREADS + wave * 64) * 8);
-      load_lds16(src + v_off + vchk[i] * 8, Vs[buf] + (i * PF_THREADS + wave * 64) * 8);
+      load_lds16(src + kchk[i] * 8, kd + i * PF_THREADS * 16);
+      load_lds16(src + v_off + vchk[i] * 8, vd + i * PF_THREADS * 16);
     }
   };
 
+  u32x4 qb[KSTEPS];  // Q^T operand, loaded in the prologue
   f32x16 oacc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
@@ -207,53 +221,54 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   const int vkey_in = 4 * (tg >> 1) + tj;                  // + kbase (multiple of 8)
   const int vdim_in = 16 * (tg & 1) + 4 * trr;             // + 32d
 
-  // Prologue: tiles 0 .. STAGES-2 in flight, ids of tile STAGES-1 fetched.
-  int32_t ids[MAXNB];
-  fetch_ids(0, ids);
-#pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j) {
-    if (j < ntile) issue_loads(j, ids, j);
-    fetch_ids(j + 1, ids);
-  }
-
-  for (int32_t t = 0; t < ntile; ++t) {
+  // QK of one tile into S^T (two 32-key blocks, chains interleaved; K fragments are
+  // streamed one k-step ahead of the MFMAs that use them).
+  auto qk = [&](int32_t t, f32x16* sacc) {
     const int buf = t % STAGES;
-    // Tile t has landed once at most (tiles issued after it) * LPT loads are pending.
-    const int32_t later = min(STAGES - 2, ntile - 1 - t);
-    if (later >= 2) wait_vmcnt<2 * LPT>();
-    else if (later == 1) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // everyone's part of tile t is in; buffer (t - 1) % STAGES is free
-    if (t + STAGES - 1 < ntile) {
-      issue_loads(t + STAGES - 1, ids, (t + STAGES - 1) % STAGES);
-      fetch_ids(t + STAGES, ids);
-    }
-    const int32_t key0 = t * 64;
-    if (!wave_active || key0 > pmax) continue;  // nothing of this tile is visible
-    // S^T = K Q^T for keys key0 .. key0+63 (two 32-key blocks, their accumulation
-    // chains interleaved so consecutive MFMAs are independent).
-    f32x16 sacc[2];
-    {
-      u32x4 a[2][KSTEPS];
+    const uint16_t* kt = Ks[buf];
+    const int r0 = col, r1 = 32 + col;
+    auto frag = [&](int row, int s) {
+      return *(const u32x4*)(kt + (row * CPR + ((2 * s + hl) ^ kswz<CPR>(row))) * 8);
+    };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int krow_r = 32 * kb + col;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          a[kb][s] = *(const u32x4*)(Ks[buf] +
-                                     (krow_r * CPR + ((2 * s + hl) ^ kswz<CPR>(krow_r))) * 8);
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    u32x4 a0 = frag(r0, 0), a1 = frag(r1, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    for (int s = 0; s < KSTEPS; ++s) {
+      u32x4 n0 = a0, n1 = a1;
+      if (s + 1 < KSTEPS) {
+        n0 = frag(r0, s + 1);
+        n1 = frag(r1, s + 1);
       }
-      __builtin_amdgcn_s_setprio(1);  // let the other wave's softmax fill the MFMA shadow
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kb][s]),
-                                                            as_bf16x8(qb[s]), sacc[kb], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qb[s]), sacc[0],
+                                                        0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qb[s]), sacc[1],
+                                                        0, 0, 0);
+      a0 = n0;
+      a1 = n1;
     }
+  };
+  // The two transposing reads that form the V^T fragment of step (kb, s2), dim block d.
+  auto vfrag = [&](const uint16_t* vt, int step, int d) {
+    const int kbase = 16 * step;  // step = 2 kb + s2: keys 32kb + 16s2
+    const int r0 = kbase + vkey_in, r1 = r0 + 8;
+    const int dim = 32 * d + vdim_in;
+    const int u = dim >> 3, half = dim & 7;
+    const u32x2 lo = ds_read_tr(vt + (r0 * CPR + (u ^ vswz<CPR>(r0))) * 8 + half);
+    const u32x2 hi = ds_read_tr(vt + (r1 * CPR + (u ^ vswz<CPR>(r1))) * 8 + half);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+  };
+  // Mask, online softmax and P.V of one tile whose scores are in sacc.
+  auto softmax_pv = [&](int32_t t, f32x16* sacc) {
+    const int buf = t % STAGES;
+    const uint16_t* vt = Vs[buf];
+    const int32_t key0 = t * 64;
+    // V fragments of the first P.V step go into flight before the softmax arithmetic.
+    u32x4 va[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) va[d] = vfrag(vt, 0, d);
     // Causal mask where the tile reaches past the wave's first position; running
     // max.  Register r of block kb holds key 32kb + 8(r/4) + 4hl + r%4.
     if (key0 + 63 > pmin) {
@@ -270,7 +285,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = pair_max(mt);  // the other half of this row's keys lives 32 lanes away
     const float mn = fmaxf(m_run, mt * scale_log2);
     if (__any(mn != m_run)) {  // rescale only when some running max moved
       const float alpha = fast_exp2(m_run - mn);
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
       m_run = mn;
     }
     float psum = 0.f;
-    u32x4 pb[2][2];
+    u32x4 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
@@ -293,44 +308,75 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        pb[kb][s2].x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
-        pb[kb][s2].y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
-        pb[kb][s2].z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
-        pb[kb][s2].w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
+        pb[2 * kb + s2].x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
+        pb[2 * kb + s2].y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
+        pb[2 * kb + s2].z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
+        pb[2 * kb + s2].w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
       }
     }
     l_run += psum;
-
-    // O^T += V^T P^T.  MFMA k index 8*hl + j maps to key 32kb + 16s2 + 8(j/4) + 4hl + j%4,
-    // the same keys this lane's P registers 8s2 .. 8s2+7 hold; the two transposing reads
-    // fetch those keys (kbase + 4hl + 0..3 and kbase + 8 + 4hl + 0..3) at dim 32d + col.
+    // O^T += V^T P^T over the four 16-key steps; MFMA k index 8*hl + j maps to key
+    // 32kb + 16s2 + 8(j/4) + 4hl + j%4, the keys this lane's P registers hold.  The next
+    // step's V fragments are read while this step's MFMAs run.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int step = 0; step < 4; ++step) {
+      u32x4 vn[DB];
+      if (step + 1 < 4) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kbase = 32 * kb + 16 * s2;
-        const int r0 = kbase + vkey_in, r1 = r0 + 8;
-        u32x4 a[DB];
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const int dim = 32 * d + vdim_in;
-          const int u = dim >> 3, half = dim & 7;
-          const u32x2 lo = ds_read_tr(Vs[buf] + (r0 * CPR + (u ^ vswz<CPR>(r0))) * 8 + half);
-          const u32x2 hi = ds_read_tr(Vs[buf] + (r1 * CPR + (u ^ vswz<CPR>(r1))) * 8 + half);
-          a[d] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[d]),
-                                                           as_bf16x8(pb[kb][s2]), oacc[d],
-                                                           0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
+        for (int d = 0; d < DB; ++d) vn[d] = vfrag(vt, step + 1, d);
       }
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[d]), as_bf16x8(pb[step]),
+                                                         oacc[d], 0, 0, 0);
+      if (step + 1 < 4) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d) va[d] = vn[d];
+      }
+    }
+  };
+  auto active = [&](int32_t t) { return wave_active && t < ntile && t * 64 <= pmax; };
+
+  // Prologue: tiles 0 .. STAGES-2 in flight; QK of tile 0 once it has landed.
+  int32_t ids[MAXNB];
+  fetch_ids(0, ids);
+#pragma unroll
+  for (int j = 0; j < STAGES - 1; ++j) {
+    if (j < ntile) issue_loads(j, ids, j);
+    fetch_ids(j + 1, ids);
+  }
+  // Q^T operand: k-step s holds dims 16s + 8*hl .. +8 of this lane's row.  Loaded after
+  // the first tiles so that one full wait covers both: afterwards no register load is
+  // outstanding, and every vector-memory operation in the loop is a tile load whose
+  // completion the loop tracks with its own vmcnt waits.
+  {
+    const uint16_t* qr = qkv + ((size_t)(tok0 + rtok) * (Hq + 2 * Hkv) + rhead) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qb[s] = ld16(qr + 16 * s + 8 * hl);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 s_cur[2], s_next[2];
+  if (active(0)) qk(0, s_cur);
+
+  for (int32_t t = 0; t < ntile; ++t) {
+    // Tiles t and t+1 resident: at most the tile issued last (t + STAGES - 2) pending.
+    if (t + STAGES - 2 < ntile) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // buffer (t - 1) % STAGES is free for tile t + STAGES - 1
+    if (t + STAGES - 1 < ntile) {
+      issue_loads(t + STAGES - 1, ids, (t + STAGES - 1) % STAGES);
+      fetch_ids(t + STAGES, ids);
+    }
+    // QK of the next tile goes to the matrix cores while this tile's softmax runs.
+    if (active(t + 1)) qk(t + 1, s_next);
+    if (active(t)) softmax_pv(t, s_cur);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
   }
 
   if (!row_valid) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.f / l_tot;
   uint16_t* orow = out + ((size_t)(tok0 + rtok) * Hq + rhead) * D;
 #pragma unroll
@@ -352,7 +398,6 @@ hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
   const int32_t n_groups = b.n_prefill_seqs * s.n_kv_heads;
   const int32_t grid = ((n_groups + N_XCD - 1) / N_XCD) * b.prefill_qtiles_max * N_XCD;
   const int32_t qtt = q_tile_tokens(s.n_q_heads / s.n_kv_heads);
-  static_assert(STAGES - 2 <= 2, "wait_vmcnt cases cover up to two later tiles");
   hipLaunchKernelGGL((prefill_attn_kernel<D>), dim3(grid), dim3(PF_THREADS), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out,
                      (const int4*)b.prefill_work, n_groups, b.prefill_qtiles_max, qtt,
