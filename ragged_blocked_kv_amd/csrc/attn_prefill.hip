@@ -27,6 +27,8 @@
 #include "rbkv_device.h"
 #include "rbkv_internal.h"
 
+#include <type_traits>
+
 namespace rbkv {
 namespace {
 
@@ -98,14 +100,16 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     int32_t qtt, const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
     int32_t Hkv, int32_t G, int32_t bs, float scale_log2) {
-  constexpr int CPR = D / 8;               // 16-byte chunks per key row
-  constexpr int TILE_CHUNKS = 64 * CPR;    // chunks per K (or V) tile
-  constexpr int NLD = TILE_CHUNKS / PF_THREADS;  // direct loads per thread per K (or V) tile
-  constexpr int LPT = 2 * NLD;             // vector-memory operations per thread per tile
-  constexpr int KSTEPS = D / 16;           // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;               // 32-wide dim blocks of the output
-  constexpr int MAXNB = 4;                 // blocks a 64-key tile can span (block size 16)
-  static_assert(NLD >= 1, "tile smaller than the workgroup");
+  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  constexpr int TILE_CHUNKS = 64 * CPR;        // chunks per K (or V) tile
+  constexpr int LOADERS = PF_THREADS / 2;      // threads of the loading group
+  constexpr int NLD = TILE_CHUNKS / LOADERS;   // direct loads per loader per K (or V) tile
+  constexpr int LPT = 2 * NLD;                 // vector-memory operations per loader per tile
+  constexpr int ROWS_PER_LD = LOADERS / CPR;   // key rows between a loader's loads (16 or 32)
+  constexpr int KSTEPS = D / 16;               // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                   // 32-wide dim blocks of the output
+  constexpr int MAXNB = 4;                     // blocks a 64-key tile can span (block size 16)
+  static_assert(NLD >= 1 && ROWS_PER_LD % 16 == 0, "loader geometry");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[STAGES][64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[STAGES][64 * D];
 
@@ -128,6 +132,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  // Wave w and wave w + 4 of a workgroup share a SIMD: group 0 (waves 0-3) and group 1
+  // (waves 4-7) take turns on each SIMD's matrix core.
+  const int32_t grp = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int hl = lane >> 5;     // half of the wave
   const int col = lane & 31;    // query row within the wave's 32
 
@@ -149,25 +156,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   const int32_t rr = row_valid ? row : rows - 1;
   const int32_t rtok = rr / G, rhead = kvh * G + rr % G;
   const int32_t rpos = seen + q0 + rtok;
-  // Rows spanned by this wave, for tile skipping and mask-free tiles.
-  const int32_t w_lo = wave * 32;
-  const bool wave_active = w_lo < rows;
-  const int32_t w_hi = min(rows, w_lo + 32) - 1;
-  const int32_t pmin = seen + q0 + (wave_active ? w_lo / G : 0);
-  const int32_t pmax = seen + q0 + (wave_active ? w_hi / G : 0);
 
-
-  // Loader role: direct load i of this thread fills LDS chunk i*PF_THREADS + tid of a
-  // tile, which holds row (i*PF_THREADS + tid) / CPR and, after the swizzle, a chunk of
-  // that row.
-  int krow[NLD], kchk[NLD], vchk[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int pos = i * PF_THREADS + tid;
-    krow[i] = pos / CPR;
-    kchk[i] = (pos % CPR) ^ kswz<CPR>(krow[i]);
-    vchk[i] = (pos % CPR) ^ vswz<CPR>(krow[i]);
-  }
+  // Loader role (group 1).  Direct load i of loader lt fills LDS chunk i*LOADERS + lt of a
+  // tile: key row i*ROWS_PER_LD + lt/CPR and, after the swizzle, one of its chunks.  The
+  // swizzles depend on the row's low four bits only, so they are the same for every i.
+  const int lt = tid & (LOADERS - 1);
+  const int lrow = lt / CPR;
+  const int k_src = lrow * D + ((lt % CPR) ^ kswz<CPR>(lrow)) * 8;
+  const int v_src = lrow * D + ((lt % CPR) ^ vswz<CPR>(lrow)) * 8;
   // Block ids of a tile: uniform across the workgroup, so they come through the scalar
   // cache and never hold up the vector-memory queue that carries the tile data.
   auto fetch_ids = [&](int32_t t, int32_t* ids) {
@@ -178,10 +174,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   const size_t blk_stride = (size_t)2 * Hkv * head_stride;  // elements per pool block
   // LDS byte address where this wave's first direct load of a K tile lands (stage 0); a
   // V tile's sits STAGES tiles further.  Stage buf adds buf * TILE_BYTES, load i adds
-  // i * PF_THREADS * 16.
+  // i * LOADERS * 16.
   constexpr uint32_t TILE_BYTES = 64 * D * 2;
-  const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[0][0]) + wave * 64 * 16);
-  const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[0][0]) + wave * 64 * 16);
+  const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Ks[0][0]) + (wave & 3) * 64 * 16);
+  const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[0][0]) + (wave & 3) * 64 * 16);
   auto issue_loads = [&](int32_t t, const int32_t* ids, int buf) {
     const uint32_t kd = k_dst0 + buf * TILE_BYTES, vd = v_dst0 + buf * TILE_BYTES;
     if (bs >= 64 && t * 64 + 63 < n_keys) {
@@ -189,67 +185,45 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
       const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)((t * 64) % bs) * D;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const uint16_t* src = base + krow[i] * D;
-        load_lds16(src + kchk[i] * 8, kd + i * PF_THREADS * 16);
-        load_lds16(src + v_off + vchk[i] * 8, vd + i * PF_THREADS * 16);
+        load_lds16(base + i * ROWS_PER_LD * D + k_src, kd + i * LOADERS * 16);
+        load_lds16(base + v_off + i * ROWS_PER_LD * D + v_src, vd + i * LOADERS * 16);
       }
       return;
     }
     const int32_t b0 = (t * 64) / bs;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int32_t key = min(t * 64 + krow[i], n_keys - 1);  // rows past the end: last key
+      // Rows past the end load the last key (never read unmasked).
+      const int32_t key = min(t * 64 + i * ROWS_PER_LD + lrow, n_keys - 1);
       const int jb = key / bs - b0;
       const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
-      const uint16_t* src = pool_g + (size_t)id * blk_stride + (size_t)(key % bs) * D;
-      load_lds16(src + kchk[i] * 8, kd + i * PF_THREADS * 16);
-      load_lds16(src + v_off + vchk[i] * 8, vd + i * PF_THREADS * 16);
+      const uint16_t* src = pool_g + (size_t)id * blk_stride + (size_t)(key % bs) * D - lrow * D;
+      load_lds16(src + k_src, kd + i * LOADERS * 16);
+      load_lds16(src + v_off + v_src, vd + i * LOADERS * 16);
     }
   };
 
-  u32x4 qb[KSTEPS];  // Q^T operand, loaded in the prologue
+  u32x4 qb[KSTEPS];  // Q^T operand: k-step s holds dims 16s + 8*hl .. +8 of this lane's row
   f32x16 oacc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16 sacc[2];  // S^T of the current tile: block kb holds keys 32kb .. 32kb+31
+  u32x4 pb[4];     // its weights in bf16, P^T operand of the four 16-key steps
 
   // Transposing-read addresses of the V^T fragments (element offsets into a V tile):
   // source lane 16g + 4j + r reads key kbase + 4(g/2) + j, dims 32d + 16(g%2) + 4r .. +4.
   const int tg = lane >> 4, tj = (lane >> 2) & 3, trr = lane & 3;
   const int vkey_in = 4 * (tg >> 1) + tj;                  // + kbase (multiple of 8)
   const int vdim_in = 16 * (tg & 1) + 4 * trr;             // + 32d
+  // K fragment of k-step s for key row col (row 32 + col sits 32 rows further: the
+  // swizzle depends on the row's low bits only): element offset in a K tile.
+  int koff[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = (col * CPR + ((2 * s + hl) ^ kswz<CPR>(col))) * 8;
 
-  // QK of one tile into S^T (two 32-key blocks, chains interleaved; K fragments are
-  // streamed one k-step ahead of the MFMAs that use them).
-  auto qk = [&](int32_t t, f32x16* sacc) {
-    const int buf = t % STAGES;
-    const uint16_t* kt = Ks[buf];
-    const int r0 = col, r1 = 32 + col;
-    auto frag = [&](int row, int s) {
-      return *(const u32x4*)(kt + (row * CPR + ((2 * s + hl) ^ kswz<CPR>(row))) * 8);
-    };
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    u32x4 a0 = frag(r0, 0), a1 = frag(r1, 0);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      u32x4 n0 = a0, n1 = a1;
-      if (s + 1 < KSTEPS) {
-        n0 = frag(r0, s + 1);
-        n1 = frag(r1, s + 1);
-      }
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qb[s]), sacc[0],
-                                                        0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qb[s]), sacc[1],
-                                                        0, 0, 0);
-      a0 = n0;
-      a1 = n1;
-    }
-  };
   // The two transposing reads that form the V^T fragment of step (kb, s2), dim block d.
   auto vfrag = [&](const uint16_t* vt, int step, int d) {
     const int kbase = 16 * step;  // step = 2 kb + s2: keys 32kb + 16s2
@@ -260,26 +234,86 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     const u32x2 hi = ds_read_tr(vt + (r1 * CPR + (u ^ vswz<CPR>(r1))) * 8 + half);
     return u32x4{lo.x, lo.y, hi.x, hi.y};
   };
-  // Mask, online softmax and P.V of one tile whose scores are in sacc.
-  auto softmax_pv = [&](int32_t t, f32x16* sacc) {
-    const int buf = t % STAGES;
-    const uint16_t* vt = Vs[buf];
-    const int32_t key0 = t * 64;
-    // V fragments of the first P.V step go into flight before the softmax arithmetic.
-    u32x4 va[DB];
+  // Matrix-core block: S^T of tile t (two 32-key blocks, k-step chains alternating), then
+  // O^T += V^T P^T of tile t-1.  For P.V, MFMA k index 8*hl + j of step (kb, s2) is key
+  // 32kb + 16s2 + 8(j/4) + 4hl + j%4: exactly the keys this lane's P registers hold.
+  // LDS reads run a fixed distance ahead of the MFMAs that use them (K: two k-steps,
+  // V: one fragment per MFMA); scheduling fences keep the compiler from hoisting them
+  // further, which would only cost registers.
+  auto mblock = [&](int32_t t, auto do_qk, auto do_pv) {
+    constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
+    const uint16_t* kt = Ks[t % STAGES];
+    const uint16_t* vt = Vs[(t + STAGES - 1) % STAGES];
+    auto kfrag = [&](int s, int half) { return *(const u32x4*)(kt + koff[s] + half * 32 * D); };
+    u32x4 vc[DB];
+    if constexpr (QK) {
+      u32x4 k0[3], k1[3];  // ring of K fragments: k-steps s, s+1, s+2
+      k0[0] = kfrag(0, 0);
+      k1[0] = kfrag(0, 1);
+      k0[1] = kfrag(1, 0);
+      k1[1] = kfrag(1, 1);
 #pragma unroll
-    for (int d = 0; d < DB; ++d) va[d] = vfrag(vt, 0, d);
-    // Causal mask where the tile reaches past the wave's first position; running
-    // max.  Register r of block kb holds key 32kb + 8(r/4) + 4hl + r%4.
-    if (key0 + 63 > pmin) {
+      for (int s = 0; s < KSTEPS; ++s) {
+        if (s + 2 < KSTEPS) {
+          k0[(s + 2) % 3] = kfrag(s + 2, 0);
+          k1[(s + 2) % 3] = kfrag(s + 2, 1);
+        } else if (PV) {
+          // The first P.V step's V fragments take the place of the K reads.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > rpos) sacc[kb][r] = -INFINITY;
+          for (int d = (s + 2 - KSTEPS) * DB / 2; d < (s + 3 - KSTEPS) * DB / 2; ++d)
+            vc[d] = vfrag(vt, 0, d);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(k0[s % 3]), as_bf16x8(qb[s]), s == 0 ? f32x16{} : sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(k1[s % 3]), as_bf16x8(qb[s]), s == 0 ? f32x16{} : sacc[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) vc[d] = vfrag(vt, 0, d);
     }
+    if constexpr (PV) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        u32x4 vn[DB];
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          if (st + 1 < 4) vn[d] = vfrag(vt, st + 1, d);
+          __builtin_amdgcn_sched_barrier(0);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vc[d]), as_bf16x8(pb[st]),
+                                                           oacc[d], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (st + 1 < 4) {
+#pragma unroll
+          for (int d = 0; d < DB; ++d) vc[d] = vn[d];
+        }
+      }
+    }
+  };
+  // Causal mask (bottom-right): register r of block kb holds key t*64 + 32kb + 8(r/4) +
+  // 4hl + r%4, which this lane's query (position rpos) sees iff it is <= rpos.
+  auto mask_tile = [&](int32_t t) {
+    const int32_t lim = rpos - t * 64 - 4 * hl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+  };
+  // Tiles t < t_free are visible to every query of the item (t*64 + 63 <= seen + q0).
+  const int32_t t_free = (seen + q0 + 1) >> 6;
+  // Online softmax of tile t: mask, running maximum, weights 2^(s*scale - m), their sum
+  // and bf16 packing.  The running maximum m moves only when some row's maximum exceeds
+  // it by more than RESCALE_SLACK (log2 units): weights then stay below 2^RESCALE_SLACK
+  // and O and l are rescaled rarely.  The result is the same softmax; only the common
+  // factor that the partial sums carry differs.  The first tile always moves m (from
+  // -inf: key 0 is visible to every row, so its maximum is finite).
+  constexpr float RESCALE_SLACK = 8.f;
+  auto softmax = [&](int32_t t) {
+    if (t >= t_free) mask_tile(t);
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -287,7 +321,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
     mt = pair_max(mt);  // the other half of this row's keys lives 32 lanes away
     const float mn = fmaxf(m_run, mt * scale_log2);
-    if (__any(mn != m_run)) {  // rescale only when some running max moved
+    if (__any(mn > m_run + RESCALE_SLACK)) {
       const float alpha = fast_exp2(m_run - mn);
       l_run *= alpha;
 #pragma unroll
@@ -297,83 +331,86 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
       m_run = mn;
     }
     float psum = 0.f;
-    u32x4 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_run));
-        psum += p[r];
-      }
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        pb[2 * kb + s2].x = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
-        pb[2 * kb + s2].y = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
-        pb[2 * kb + s2].z = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
-        pb[2 * kb + s2].w = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = fast_exp2(fmaf(sacc[kb][8 * s2 + j], scale_log2, -m_run));
+          psum += p[j];
+        }
+        pb[2 * kb + s2] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
       }
-    }
     l_run += psum;
-    // O^T += V^T P^T over the four 16-key steps; MFMA k index 8*hl + j maps to key
-    // 32kb + 16s2 + 8(j/4) + 4hl + j%4, the keys this lane's P registers hold.  The next
-    // step's V fragments are read while this step's MFMAs run.
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      u32x4 vn[DB];
-      if (step + 1 < 4) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d) vn[d] = vfrag(vt, step + 1, d);
-      }
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[d]), as_bf16x8(pb[step]),
-                                                         oacc[d], 0, 0, 0);
-      if (step + 1 < 4) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d) va[d] = vn[d];
-      }
-    }
   };
-  auto active = [&](int32_t t) { return wave_active && t < ntile && t * 64 <= pmax; };
 
-  // Prologue: tiles 0 .. STAGES-2 in flight; QK of tile 0 once it has landed.
+  // Every wave runs the same sequence of blocks, a barrier after each:
+  //   M_0, V_0, M_1, V_1, ..., M_{n-1}, V_{n-1}, M_n        (n = ntile)
+  // with M_k = S^T of tile k (k < n) and P.V of tile k-1 (k >= 1) on the matrix core,
+  // and V_k = softmax of tile k on the VALU.  Group 1 takes one extra barrier before M_0
+  // and group 0 one after M_n, so group 1 runs one block behind: on every SIMD one wave
+  // feeds the matrix core while the other does the softmax.  In the barrier-delimited
+  // phases p = 0 .. 2n+1, group 0 runs M_k in phase 2k and group 1 in phase 2k+1.
+  //
+  // Tile loads, all by group 1: tiles 0, 1 and 2 in the prologue, tile k+3 at the start
+  // of its V_k (phase 2k+2) into the stage of tile k-1, whose last reader (group 1's
+  // M_k) ran in phase 2k+1.  After its M_k (phase 2k+1) group 1 waits for tile k+1,
+  // which group 0 reads first in phase 2k+2; tile k+2 (issued in phase 2k) may still be
+  // in flight.
   int32_t ids[MAXNB];
   fetch_ids(0, ids);
+  if (grp == 1) {
 #pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j) {
-    if (j < ntile) issue_loads(j, ids, j);
-    fetch_ids(j + 1, ids);
+    for (int j = 0; j < 3; ++j) {
+      if (j < ntile) issue_loads(j, ids, j);
+      fetch_ids(j + 1, ids);
+    }
   }
-  // Q^T operand: k-step s holds dims 16s + 8*hl .. +8 of this lane's row.  Loaded after
-  // the first tiles so that one full wait covers both: afterwards no register load is
-  // outstanding, and every vector-memory operation in the loop is a tile load whose
-  // completion the loop tracks with its own vmcnt waits.
   {
     const uint16_t* qr = qkv + ((size_t)(tok0 + rtok) * (Hq + 2 * Hkv) + rhead) * D;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qb[s] = ld16(qr + 16 * s + 8 * hl);
   }
-  wait_vmcnt<0>();
+  // Tiles 0 and 1 and the Q^T operand resident; tile 2 may stay in flight.  Afterwards
+  // no register load is outstanding: every vector-memory operation in the loop is a
+  // tile load whose completion these waits track.
+  if (grp == 1 && ntile > 2) wait_vmcnt<LPT>();
+  else wait_vmcnt<0>();
   __syncthreads();
-  f32x16 s_cur[2], s_next[2];
-  if (active(0)) qk(0, s_cur);
+  if (grp == 1) __syncthreads();  // group 1 starts one phase behind
 
-  for (int32_t t = 0; t < ntile; ++t) {
-    // Tiles t and t+1 resident: at most the tile issued last (t + STAGES - 2) pending.
-    if (t + STAGES - 2 < ntile) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // buffer (t - 1) % STAGES is free for tile t + STAGES - 1
-    if (t + STAGES - 1 < ntile) {
-      issue_loads(t + STAGES - 1, ids, (t + STAGES - 1) % STAGES);
-      fetch_ids(t + STAGES, ids);
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  auto after_m = [&](int32_t kk) {  // group 1, end of M_kk: tile kk+1 resident
+    if (grp == 1) {
+      if (kk + 2 < ntile) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
     }
-    // QK of the next tile goes to the matrix cores while this tile's softmax runs.
-    if (active(t + 1)) qk(t + 1, s_next);
-    if (active(t)) softmax_pv(t, s_cur);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_next[kb];
+    __syncthreads();
+  };
+  auto before_v = [&](int32_t kk) {  // group 1, start of V_kk: tile kk+3 into flight
+    if (grp == 1 && kk + 3 < ntile) {
+      issue_loads(kk + 3, ids, (kk + 3) % STAGES);
+      fetch_ids(kk + 4, ids);
+    }
+  };
+  mblock(0, yes{}, no{});
+  after_m(0);
+  before_v(0);
+  softmax(0);
+  __syncthreads();
+  for (int32_t kk = 1; kk < ntile; ++kk) {
+    mblock(kk, yes{}, yes{});
+    after_m(kk);
+    before_v(kk);
+    softmax(kk);
+    __syncthreads();
   }
+  mblock(ntile, no{}, yes{});
+  if (grp == 0) __syncthreads();  // matches group 1's extra barrier
 
   if (!row_valid) return;
   const float l_tot = pair_sum(l_run);
