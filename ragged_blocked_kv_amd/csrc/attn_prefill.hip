@@ -1,24 +1,29 @@
 // Causal attention of bf16 prefill chunks on the gfx950 matrix cores.
 //
-// A work item is (sequence, kv head, a run of the chunk's tokens).  Its 128 query rows
-// are (token, head-in-group) pairs, so every K/V tile loaded into LDS serves all G query
-// heads of the kv group.  Each of the 4 wavefronts owns 32 rows and runs
-//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, keys x rows, K from LDS, Q held in registers)
-//   online softmax down each column (the lane owns one row: a column max is 16 register
+// A workgroup takes one work item: (sequence, kv head, a run of up to 256/G of the chunk's
+// tokens).  Its 256 query rows are (token, head-in-group) pairs, so every K/V tile in LDS
+// serves all G query heads of the kv group.  Eight wavefronts own 32 rows each and, per
+// 64-key tile, compute
+//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, keys x rows, K from LDS, Q in registers),
+//   an online softmax down each column (a lane owns one row: a column max is 16 register
 //                 maxima plus one exchange with the partner lane 32 away),
-//   O^T += V^T P^T (same instruction; P comes straight from the S^T accumulators, the
-//                 V^T fragments from transposing LDS reads, ds_read_b64_tr_b16),
-// over 64-key tiles, with the causal mask applied bottom-right (query at position p sees
-// keys 0..p, p = seen + offset in the chunk) and only on the tiles that need it.
+//   O^T += V^T P^T (same instruction; P comes straight from the S^T accumulators, the V^T
+//                 fragments from transposing LDS reads, ds_read_b64_tr_b16),
+// with the causal mask applied bottom-right (the query at position p sees keys 0..p,
+// p = seen + offset in the chunk) on the tiles that reach the diagonal only.
 //
-// Data movement: K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
-// no staging registers), double-buffered with one barrier per tile; the next tile is
-// in flight while the current one is computed, and block ids are fetched one tile
-// further ahead.  Each lane's source address is chosen so that the LDS image carries an
-// XOR swizzle: K fragments (16 consecutive rows, one 16-byte chunk each) and transposed
-// V reads (8 keys x 32 dims per instruction) are both free of bank conflicts.  Work
-// items are mapped onto block indices so that the query tiles of one (sequence,
-// kv head) run on the same XCD and share its L2.
+// Scheduling: waves w and w + 4 share a SIMD.  The two groups (waves 0-3, 4-7) alternate
+// between a matrix-core block (S^T of tile k and P.V of tile k-1) and a VALU block (the
+// softmax of tile k), one block apart, so each SIMD's matrix core is fed by one wave while
+// the other computes weights; the matrix-core block runs at raised issue priority.
+//
+// Data movement: K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+// staging registers) through a four-stage ring, two tiles ahead of use, issued by one
+// group during its VALU block; block ids come through the scalar cache two tiles ahead of
+// that.  Each lane's source address is chosen so that the LDS image carries an XOR
+// swizzle: K fragments (16 consecutive rows, one 16-byte chunk each) and transposing V
+// reads are both free of bank conflicts.  Work items are mapped onto block indices so that
+// the query tiles of one (sequence, kv head) run on the same XCD and share its L2.
 //
 // Dynamic SplitFuse chunks continuing a sequence with seen cached tokens:
 // "DeepSpeed-Inference and DeepSpeed-MII", sections 10.3 and 10.10; query-tile sizing per
@@ -76,8 +81,14 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
-// Max / sum of a value and its copy 32 lanes away (one v_permlane32_swap, no LDS).
-__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+// Max / sum of a value and its copy 32 lanes away.  v_permlane32_swap of a register with
+// itself hands every lane the pair (v[l % 32], v[l % 32 + 32]); being a VALU operation it
+// does not wait on the LDS/scalar-memory counter that the scalar block-id loads in flight
+// also hold.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
 __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
@@ -242,6 +253,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   // further, which would only cost registers.
   auto mblock = [&](int32_t t, auto do_qk, auto do_pv) {
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
+    // The SIMD's other wave runs its softmax meanwhile: issue priority goes to this
+    // block, so the matrix core is fed first and the VALU work fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
     const uint16_t* kt = Ks[t % STAGES];
     const uint16_t* vt = Vs[(t + STAGES - 1) % STAGES];
     auto kfrag = [&](int s, int half) { return *(const u32x4*)(kt + koff[s] + half * 32 * D); };
@@ -292,6 +306,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   // Causal mask (bottom-right): register r of block kb holds key t*64 + 32kb + 8(r/4) +
   // 4hl + r%4, which this lane's query (position rpos) sees iff it is <= rpos.
