@@ -325,6 +325,214 @@ void decode_attn_kernel(
   }
 }
 
+// Grouped-query decode for bf16 caches: one wavefront per query head of the kv group
+// (NW >= G waves; waves past G repeat the last head and write nothing).  Each 64-key K/V
+// tile is loaded once per workgroup, straight from HBM into LDS (global_load_lds), and
+// every wave streams its own head over it: Q in registers, one key per lane for Q.K (K
+// rows XOR-swizzled in LDS), a wave-level online softmax, and P.V with lanes over
+// head-dim chunks (two keys per v_dot2_f32_bf16).  Two LDS stages (the next tile loads
+// while this one is computed) keep the workgroup at 66 KB and its waves at 128 registers,
+// so two workgroups share a CU: what hides the memory latency here is the number of
+// independent waves, not a deeper prefetch.  The work item, the split-K partition and
+// the partial layout are those of the per-wave kernel above.
+template <int D, int NW, bool ONE_BLK>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_group_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
+    uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
+    const int32_t* __restrict__ tok2seq, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int NT = NW * 64;                // threads
+  constexpr int TILE_CHUNKS = 64 * CPR;      // chunks per K (or V) tile
+  constexpr int LDT = NT < TILE_CHUNKS ? NT : TILE_CHUNKS;  // loading threads (whole waves)
+  constexpr int NLD = TILE_CHUNKS / LDT;     // direct loads per loading thread per K (or V) tile
+  constexpr int KPI = 64 / CPR;              // P.V: keys per row group (lanes per chunk column)
+  constexpr int NI = CPR;                    // P.V: row groups per tile
+  constexpr int STG = 2;                     // tiles resident: one computed, one in flight
+  constexpr int MAXNB = 4;                   // blocks a 64-key tile can span (block size 16)
+  static_assert(TILE_CHUNKS % LDT == 0 && LDT % 64 == 0, "loader geometry");
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[STG][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[STG][64 * D];
+  __shared__ float ps[NW][64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int4 w = work[blockIdx.x];
+  const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
+  const int32_t seq = tok2seq[token];
+  const int32_t nkeys = pos[token] + 1;
+  const int32_t tiles_total = (nkeys + 63) >> 6;
+  const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
+  const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
+  const int32_t key_end = min(nkeys, t_end * 64);
+  const int32_t* bids = block_ids + block_off[seq];
+  const int bsh = 31 - __builtin_clz(bs);  // block sizes are powers of two
+  const int32_t last_blk = (key_end - 1) >> bsh;
+  const size_t head_stride = (size_t)bs * D;
+  const size_t blk_stride = (size_t)2 * Hkv * head_stride;
+  const size_t v_off = (size_t)Hkv * head_stride;
+  const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
+  // This wave's head within the group; uniform, so its query row comes through the scalar
+  // cache and no register load is pending while the tile loads are in flight.
+  const int32_t hg = min(wave, G - 1);
+
+  // Loader: direct load i of thread tid fills LDS chunk p = i*LDT + tid of a tile, i.e.
+  // key row p / CPR.  K chunks carry an XOR swizzle (chunk c of row r at c ^ swz(r)) so
+  // that the one-row-per-lane Q.K reads are free of bank conflicts; V rows are stored as
+  // they are (a P.V read covers whole rows).
+  auto kswz = [](int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); };
+  auto fetch_ids = [&](int32_t t, int32_t* ids) {
+    const int32_t b0 = min((t * 64) >> bsh, last_blk);
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j) ids[j] = bids[min(b0 + j, last_blk)];
+  };
+  constexpr uint32_t TILE_BYTES = 64 * D * 2;
+  const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[0][0]) + wave * 64 * 16);
+  const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vt[0][0]) + wave * 64 * 16);
+  auto issue_tile = [&](int32_t t, const int32_t* ids, int buf) {
+    if (LDT < NT && tid >= LDT) return;  // waves past the tile's chunk count load nothing
+    const int32_t key0 = t * 64;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int p = i * LDT + tid;
+      const int r = p / CPR, c = p % CPR;
+      // Rows past the end of the split load its last key (never read unmasked).
+      int32_t k = min(key0 + r, key_end - 1);
+      const uint16_t* row;
+      if constexpr (ONE_BLK) {
+        row = pool_g + (size_t)ids[0] * blk_stride + (size_t)(k & (bs - 1)) * D;
+      } else {
+        const int jb = (k >> bsh) - (key0 >> bsh);
+        const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
+        row = pool_g + (size_t)id * blk_stride + (size_t)(k & (bs - 1)) * D;
+      }
+      const uint32_t off = buf * TILE_BYTES + i * LDT * 16;
+      load_lds16(row + (c ^ kswz(r)) * 8, k_dst0 + off);
+      load_lds16(row + v_off + c * 8, v_dst0 + off);
+    }
+  };
+
+  // This wave's query row in registers: chunk c holds dims 8c .. 8c+7.
+  u32x4 q[CPR];
+  {
+    const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + hg) * D;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) q[c] = ld16(qrow + c * 8);
+  }
+  int32_t ids[MAXNB];
+  fetch_ids(t_begin, ids);
+  issue_tile(t_begin, ids, 0);
+  fetch_ids(min(t_begin + 1, t_end - 1), ids);
+  wait_vmcnt<0>();  // Q and the first tile; afterwards only tile loads are in flight
+  __syncthreads();
+
+  float m_run = -INFINITY, lsum = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  const int cl = lane % CPR, kg = lane / CPR;  // P.V: chunk column and key sub-row
+  const int kchunk0 = lane * CPR;              // Q.K: this lane's key row (in chunks)
+
+  for (int32_t tt = t_begin; tt < t_end; ++tt) {
+    const int j = tt - t_begin;
+    if (j > 0) {
+      // Tile tt resident (the only load in flight); every wave past tile tt-1, whose
+      // stage takes tile tt+1.
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if (tt + 1 < t_end) {
+      issue_tile(tt + 1, ids, (j + 1) % STG);
+      fetch_ids(min(tt + 2, t_end - 1), ids);
+    }
+    const u32x4* kt = (const u32x4*)Kt[j % STG];
+    const u32x4* vt = (const u32x4*)Vt[j % STG];
+    const int32_t key0 = tt * 64;
+
+    // Scores: lane = key.
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) s = dot_chunk(q[c], kt[kchunk0 + (c ^ kswz(lane))], s, bf16_t{});
+    const float sc = key0 + lane < key_end ? s * scale_log2 : -INFINITY;
+    const float mn = fmaxf(m_run, wave_max_dpp(sc));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+    const float pe = __builtin_amdgcn_exp2f(sc - mn);
+    m_run = mn;
+    lsum = lsum * alpha + pe;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+    ps[wave][lane] = pe;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P.V: lane accumulates the 8 columns of chunk cl over keys i*KPI + kg, two keys per
+    // v_dot2 (rows i and i+1 interleaved per column with v_perm_b32); the weight of key r
+    // comes from lane r.
+#pragma unroll
+    for (int i = 0; i < NI; i += 2) {
+      const int ra = i * KPI + kg, rb = ra + KPI;
+      const u32x4 a = vt[ra * CPR + cl], b = vt[rb * CPR + cl];
+      const bf16x2v pp = as_bf16x2(pack_bf16x2(ps[wave][ra], ps[wave][rb]));
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        o[2 * jj] = __builtin_amdgcn_fdot2_f32_bf16(
+            pp, as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x05040100u)), o[2 * jj], false);
+        o[2 * jj + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+            pp, as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x07060302u)), o[2 * jj + 1], false);
+      }
+    }
+  }
+
+  // Reduce over the lanes that share a chunk column, and the row sums over all lanes.
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1) o[e] += __shfl_xor(o[e], off, 64);
+  lsum = wave_sum_dpp(lsum);
+  if (wave >= G) return;  // padding head
+  if (slot < 0) {
+    if (lane < CPR) {
+      const float inv = 1.f / lsum;
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = o[e] * inv;
+      st16(out + ((size_t)token * Hq + (size_t)kvh * G + hg) * D + cl * 8, pack_chunk<bf16_t>(r));
+    }
+  } else {
+    float* part = ws + (size_t)slot * G * (D + 2);
+    if (lane == 0) {
+      part[hg] = m_run;
+      part[G + hg] = lsum;
+    }
+    if (lane < CPR) {
+      float* dst = part + 2 * G + (size_t)hg * D + cl * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = o[e];
+    }
+  }
+}
+
+template <int D, int NW>
+hipError_t launch_group(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                        const void* pool, void* out, float* ws, hipStream_t stream) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  const int G = s.n_q_heads / s.n_kv_heads;
+  if (s.block_size >= 64)
+    hipLaunchKernelGGL((decode_group_kernel<D, NW, true>), dim3(b.n_decode_items), dim3(NW * 64),
+                       0, stream, (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
+                       (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
+                       b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
+                       scale_log2);
+  else
+    hipLaunchKernelGGL((decode_group_kernel<D, NW, false>), dim3(b.n_decode_items),
+                       dim3(NW * 64), 0, stream, (const uint16_t*)qkv, (const uint16_t*)pool,
+                       (uint16_t*)out, ws, (const int4*)b.decode_work, b.token_to_seq, b.pos,
+                       b.block_offsets, b.block_ids, s.n_q_heads, s.n_kv_heads, G,
+                       s.block_size, b.split_tiles, scale_log2);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int GMAX>
 hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
                     void* out, float* ws, hipStream_t stream) {
@@ -349,6 +557,11 @@ template <typename T, int D>
 hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
                     void* out, float* ws, hipStream_t stream) {
   const int G = s.n_q_heads / s.n_kv_heads;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 groups of 5 or more heads: one wave per head over shared LDS tiles.
+    if (G > 4 && G <= 8) return launch_group<D, 8>(s, b, qkv, pool, out, ws, stream);
+    if (G > 8) return launch_group<D, 16>(s, b, qkv, pool, out, ws, stream);
+  }
   if (G <= 1) return launch_t<T, D, 1>(s, b, qkv, pool, out, ws, stream);
   if (G <= 2) return launch_t<T, D, 2>(s, b, qkv, pool, out, ws, stream);
   if (G <= 4) return launch_t<T, D, 4>(s, b, qkv, pool, out, ws, stream);

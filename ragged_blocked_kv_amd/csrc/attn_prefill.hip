@@ -65,22 +65,6 @@ __device__ __forceinline__ bf16x8v as_bf16x8(u32x4 v) { return __builtin_bit_cas
 // softmax weights under 2^-126 of the running maximum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// HBM -> LDS without registers (global_load_lds_dwordx4): lane l writes its 16 bytes at
-// LDS byte address m0 + 16*l, m0 = lds (wave-uniform).  Written as inline assembly so the
-// compiler does not track the LDS write: it cannot tell the ring stages apart and would
-// otherwise wait for every load in flight before each LDS read, which serialises the
-// tile pipeline.  The kernel orders these writes against its reads itself (explicit
-// vmcnt waits, then a workgroup barrier).  The compiler writes m0 for the operand; one
-// wait state separates that write from the load that uses it.
-__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
-}
-
 // Max / sum of a value and its copy 32 lanes away.  v_permlane32_swap of a register with
 // itself hands every lane the pair (v[l % 32], v[l % 32 + 32]); being a VALU operation it
 // does not wait on the LDS/scalar-memory counter that the scalar block-id loads in flight
@@ -94,14 +78,6 @@ __device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32
 __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   return __builtin_bit_cast(u32x2, v);
-}
-
-// Wait until at most n vector-memory operations of this wave are outstanding (the LDS
-// DMA loads of later tiles stay in flight); expcnt and lgkmcnt are left alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int D>

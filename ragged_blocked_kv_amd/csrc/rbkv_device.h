@@ -110,4 +110,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// HBM -> LDS without registers (global_load_lds_dwordx4): lane l writes its 16 bytes at
+// LDS byte address m0 + 16*l, m0 = lds (wave-uniform).  Written as inline assembly so the
+// compiler does not track the LDS write: it cannot tell the ring stages apart and would
+// otherwise wait for every load in flight before each LDS read, which serialises the
+// tile pipeline.  The kernel orders these writes against its reads itself (explicit
+// vmcnt waits, then a workgroup barrier).  The compiler writes m0 for the operand; one
+// wait state separates that write from the load that uses it.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding (the LDS
+// DMA loads of later tiles stay in flight); expcnt and lgkmcnt are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace rbkv

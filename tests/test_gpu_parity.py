@@ -146,13 +146,14 @@ def test_tiny_f32_workload():
     run_full(wl, rope_base=0.0)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(14))
 def test_random_small_batches(seed):
     combos = [  # dtype, Hq, Hkv, d, bs
         ("bf16", 4, 2, 64, 16), ("bf16", 8, 8, 128, 64), ("f32", 4, 1, 64, 32),
         ("bf16", 14, 2, 128, 32), ("f32", 8, 4, 128, 128), ("bf16", 16, 1, 64, 128),
         ("bf16", 8, 2, 128, 16), ("f32", 2, 2, 64, 64), ("bf16", 6, 2, 64, 64),
         ("bf16", 32, 8, 128, 64), ("f32", 4, 4, 128, 16), ("bf16", 3, 1, 128, 32),
+        ("bf16", 16, 2, 128, 64), ("bf16", 24, 3, 64, 16),
     ]
     dt, Hq, Hkv, d, bs = combos[seed]
     wl = W.random_workload(seed, dtype=dt, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
