@@ -72,9 +72,18 @@ def measured_traffic(kernel_file, workload):
     return rec.get("bytes_per_launch")  # bytes per launch (fetch + write), scaled
 
 
-KERNEL_FILES = {"prefill_attn_kernel": "attn_prefill.hip", "decode_attn_kernel": "attn_decode.hip",
-                "append_rotary_kernel": "append_rotary.hip", "combine_kernel": "attn_combine.hip",
-                "meta_build_kernel": "meta_build.hip"}
+# Library kernels by source file (a file may hold several kernels).
+KERNEL_FILES = {"attn_prefill.hip": ("prefill_attn_kernel",),
+                "attn_decode.hip": ("decode_attn_kernel", "decode_group_kernel"),
+                "append_rotary.hip": ("append_rotary_kernel",),
+                "attn_combine.hip": ("combine_kernel",),
+                "meta_build.hip": ("meta_build_kernel",)}
+
+
+def decode_kernel_name(wl):
+    """The decode kernel a workload runs: one wave per head for bf16 groups of 5+ heads."""
+    g = wl.n_q_heads // wl.n_kv_heads
+    return "decode_group_kernel" if wl.dtype == "bf16" and g > 4 else "decode_attn_kernel"
 
 
 def copy_calibration(nbytes, reps):
@@ -112,8 +121,8 @@ def traffic_from_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, ca
     f_scale = cal_bytes / (big(cf) * 1024.0)
     w_scale = cal_bytes / (big(cw) * 1024.0)
     rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
-    for kname, kfile in KERNEL_FILES.items():
-        sel = lambda n, k=kname: k in n
+    for kfile, knames in KERNEL_FILES.items():
+        sel = lambda n, ks=knames: any(k in n for k in ks)
         fv = list(_counter_per_dispatch(fetch_csv, "FETCH_SIZE", sel).values())
         wv = list(_counter_per_dispatch(write_csv, "WRITE_SIZE", sel).values())
         if not fv or not wv:
@@ -282,7 +291,7 @@ def main():
                 "traffic": measured_traffic("attn_prefill.hip", wl.name),
                 "per_launch": {"flops": work["prefill_flops"], "us": phase_ms["prefill"] * 1e3}}
     else:
-        roof = {"kernel": "decode_attn_kernel", "bound": "hbm", "achieved": dec_gbs,
+        roof = {"kernel": decode_kernel_name(wl), "bound": "hbm", "achieved": dec_gbs,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                 "traffic": measured_traffic("attn_decode.hip", wl.name),
                 "per_launch": {"bytes": work["decode_bytes"], "us": phase_ms["decode"] * 1e3}}
