@@ -188,6 +188,50 @@ def cpu_baseline(wl, qkv_cpu, hist_fn, budget_s):
     }
 
 
+def ledger_cost(wl, eng, stream, reps=20):
+    """Host time of the native ledger around one pass of the bench batch: the batch's
+    sequences are first given their cached tokens (in groups, outside the timing), then
+    each rep runs can_schedule, put (blocks for the new tokens), the ledger's finalize
+    (host packing plus the upload, enqueued) and post_forward, as a serving loop would
+    before and after every forward pass.  Median microseconds per call."""
+    import torch
+
+    from ragged_blocked_kv_amd.state import SCHED_OK, StateManager
+
+    st = StateManager(num_blocks=wl.num_blocks, block_size=wl.block_size,
+                      max_tracked_seqs=wl.max_seqs, max_seqs=wl.max_seqs,
+                      max_tokens=1 << 20, max_context=1 << 30)
+    uids = np.arange(wl.S, dtype=np.int64) * 1_000_003 + 17
+    for g in range(0, wl.S, 16):
+        has = [i for i in range(g, min(wl.S, g + 16)) if wl.seen[i] > 0]
+        if has:
+            assert st.put(uids[has], wl.seen[has]) == SCHED_OK
+            st.post_forward()
+    n_new = wl.n_new.astype(np.int32)
+    t = {k: [] for k in ("can_schedule", "put", "finalize", "post_forward")}
+    done = 0
+    for _ in range(reps):  # the sequences grow each rep; stop when the pool is full
+        t0 = time.perf_counter()
+        ok = st.can_schedule(uids, n_new) == SCHED_OK
+        t1 = time.perf_counter()
+        if not ok:
+            break
+        done += 1
+        assert st.put(uids, n_new) == SCHED_OK
+        t2 = time.perf_counter()
+        eng.finalize_state(st, stream=stream)
+        t3 = time.perf_counter()
+        st.post_forward()
+        t4 = time.perf_counter()
+        for k, a, b in (("can_schedule", t0, t1), ("put", t1, t2), ("finalize", t2, t3),
+                        ("post_forward", t3, t4)):
+            t[k].append((b - a) * 1e6)
+        torch.cuda.synchronize()
+    med = {k: round(float(np.median(v)), 1) for k, v in t.items()}
+    return {"host_us_per_pass": med, "total_us": round(sum(med.values()), 1),
+            "sequences": wl.S, "new_tokens": wl.T, "reps": done}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +283,12 @@ def main():
     eng.finalize(wl.n_new, wl.seen, wl.block_lists, stream=stream)
     torch.cuda.synchronize()
     finalize_us = (time.perf_counter() - t0) * 1e6
+
+    # Native ledger around the same batch (host only; its finalize rewrites the device
+    # metadata, so the bench batch is finalized again afterwards).
+    ledger = ledger_cost(wl, eng, stream)
+    eng.finalize(wl.n_new, wl.seen, wl.block_lists, stream=stream)
+    torch.cuda.synchronize()
 
     # CPU-baseline inputs: the pool history of the sampled sequences, copied before the
     # first append overwrites this pass's slots.
@@ -336,6 +386,7 @@ def main():
             "attention_algorithmic_GBs": work["attention_bytes"] / (attn_ms * 1e-3) / 1e9,
         },
         "finalize_host_and_upload_us": round(finalize_us, 1),
+        "ledger": ledger,
     }
     print(json.dumps(rec), flush=True)
 

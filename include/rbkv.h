@@ -68,7 +68,8 @@ enum {
   RBKV_ERR_WORKSPACE = 5,   /* a caller buffer is smaller than the size query says */
   RBKV_ERR_DEVICE_PTR = 6,  /* buffer is not device (or pinned host) memory of the
                                current device, or its allocation is too small */
-  RBKV_ERR_HIP = 7          /* a HIP call or kernel launch failed */
+  RBKV_ERR_HIP = 7,         /* a HIP call or kernel launch failed */
+  RBKV_ERR_HOST_MEMORY = 8  /* a host allocation of the library failed */
 };
 
 enum { RBKV_DTYPE_F32 = 0, RBKV_DTYPE_BF16 = 1 };

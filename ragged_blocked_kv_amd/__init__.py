@@ -22,11 +22,11 @@ __all__ = [
     "ragged_blocked_attention_phase", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
     "PHASE_DECODE", "PHASE_COMBINE",
     "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
-    "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "DTYPE_F32", "DTYPE_BF16",
+    "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "ERR_HOST_MEMORY", "DTYPE_F32", "DTYPE_BF16",
 ]
 
 OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_BLOCKS, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
-ERR_WORKSPACE, ERR_DEVICE_PTR, ERR_HIP = 5, 6, 7
+ERR_WORKSPACE, ERR_DEVICE_PTR, ERR_HIP, ERR_HOST_MEMORY = 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16 = 0, 1
 PHASE_ALL, PHASE_PREFILL, PHASE_DECODE, PHASE_COMBINE = 0, 1, 2, 3
 
@@ -41,6 +41,24 @@ EXPORTED_SYMBOLS = (
     "blocked_kv_append_rotary",
     "ragged_blocked_attention",
     "ragged_blocked_attention_phase",
+    # include/rbkv_state.h (bound in ragged_blocked_kv_amd.state)
+    "rbkv_allocator_create",
+    "rbkv_allocator_destroy",
+    "rbkv_allocator_allocate",
+    "rbkv_allocator_free",
+    "rbkv_allocator_free_count",
+    "rbkv_state_create",
+    "rbkv_state_destroy",
+    "rbkv_state_counts",
+    "rbkv_state_sequence",
+    "rbkv_state_block_ids",
+    "rbkv_state_query",
+    "rbkv_state_can_schedule",
+    "rbkv_state_put",
+    "rbkv_state_batch",
+    "rbkv_state_finalize",
+    "rbkv_state_post_forward",
+    "rbkv_state_flush",
 )
 
 

@@ -22,6 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = [
     "api.cpp",
+    "state.cpp",
     "meta_build.hip",
     "append_rotary.hip",
     "attn_decode.hip",

@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <new>
 #include <vector>
 
 #include "rbkv_internal.h"
@@ -112,6 +113,7 @@ const char* rbkv_status_string(rbkv_status status) {
     case RBKV_ERR_WORKSPACE: return "buffer smaller than the size query requires";
     case RBKV_ERR_DEVICE_PTR: return "buffer is not memory of the expected kind on this device";
     case RBKV_ERR_HIP: return "HIP call or kernel launch failed";
+    case RBKV_ERR_HOST_MEMORY: return "host memory allocation failed";
     default: return "unknown status";
   }
 }
@@ -174,7 +176,12 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
   }
   // Block ids: in range and distinct across the batch.
   if (S > 0) {
-    std::vector<uint8_t> used((size_t)s.num_blocks, 0);
+    std::vector<uint8_t> used;
+    try {
+      used.assign((size_t)s.num_blocks, 0);
+    } catch (const std::bad_alloc&) {
+      return RBKV_ERR_HOST_MEMORY;
+    }
     for (int32_t i = 0; i < S; ++i) {
       const int64_t B_i = cdiv64((int64_t)seen[i] + n_new[i], s.block_size);
       for (int64_t k = 0; k < B_i; ++k) {

@@ -32,6 +32,7 @@ class Engine:
         self.host_pinned = torch.empty(host_b, dtype=torch.uint8, pin_memory=True)
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
         self.batch: Batch | None = None
+        self._staged = None  # event after the last upload from host_pinned
 
     @classmethod
     def for_workload(cls, wl, device="cuda"):
@@ -46,17 +47,41 @@ class Engine:
     def stream(self, stream=None):
         return torch.cuda.current_stream(self.device) if stream is None else stream
 
-    def finalize(self, n_new, seen, block_lists, stream=None) -> Batch:
-        st, b = ragged_batch_finalize(self.shape, n_new, seen, block_lists, self.host_pinned,
-                                      self.host_pinned.numel(), self.dev_meta,
-                                      self.dev_meta.numel(), self.stream(stream))
-        check(st, "ragged_batch_finalize")
+    def _staging_free(self):
+        # The pinned staging buffer is rewritten by the next finalize: wait until the
+        # stream has consumed the previous upload.
+        if self._staged is not None:
+            self._staged.synchronize()
+            self._staged = None
+
+    def _adopt(self, b: Batch, stream) -> Batch:
+        self._staged = torch.cuda.Event()
+        self._staged.record(stream)
         st, need = rbkv_workspace_bytes(self.shape, b)
         check(st, "rbkv_workspace_bytes")
         if need > self.workspace.numel():
             self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         self.batch = b
         return b
+
+    def finalize(self, n_new, seen, block_lists, stream=None) -> Batch:
+        self._staging_free()
+        stream = self.stream(stream)
+        st, b = ragged_batch_finalize(self.shape, n_new, seen, block_lists, self.host_pinned,
+                                      self.host_pinned.numel(), self.dev_meta,
+                                      self.dev_meta.numel(), stream)
+        check(st, "ragged_batch_finalize")
+        return self._adopt(b, stream)
+
+    def finalize_state(self, state, stream=None) -> Batch:
+        """Finalize the open batch of a ``state.StateManager`` ledger (its sequences, token
+        counts and block lists go straight from the native ledger to the library)."""
+        self._staging_free()
+        stream = self.stream(stream)
+        st, b = state.finalize_status(self.shape, self.host_pinned, self.host_pinned.numel(),
+                                      self.dev_meta, self.dev_meta.numel(), stream)
+        check(st, "rbkv_state_finalize")
+        return self._adopt(b, stream)
 
     def rebuild(self, stream=None, batch=None):
         check(ragged_batch_rebuild(self.shape, batch or self.batch, self.stream(stream)),

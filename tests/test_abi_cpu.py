@@ -15,9 +15,15 @@ FAKE = 0x1000  # never dereferenced: validation fails before any use
 
 
 def header_functions():
-    txt = open(os.path.join(ROOT, "include", "rbkv.h")).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", txt, flags=re.M)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        txt = open(os.path.join(inc, fn)).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", txt, flags=re.M))
+    return sorted(names)
 
 
 def shape(**kw):
@@ -51,7 +57,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for st in range(8):
+    for st in range(9):
         assert R.status_string(st) and R.status_string(st) != "unknown status"
     assert R.status_string(99) == "unknown status"
 

@@ -60,6 +60,9 @@ __all__ = [
     "make_qkv",
     "make_pool_history",
     "blocks_needed",
+    "Request",
+    "serving_trace",
+    "serving_step_qkv",
 ]
 
 
@@ -297,3 +300,46 @@ def make_pool_history(wl: Workload, device="cpu", chunk_blocks: int = 4096):
         pool[b0:b1] = torch.randn(shp, generator=g, dtype=torch.float32, device=device).to(
             pool.dtype)
     return pool
+
+
+# --------------------------------------------------------------------------------------
+# Multi-step serving traces
+# --------------------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class Request:
+    uid: int
+    arrival: int  # first step at which the request may be admitted
+    prompt: int  # prompt tokens (the first pass's chunk)
+    gen: int  # tokens generated after the prompt, one per later pass
+
+
+def serving_trace(seed: int, n_requests: int, *, max_prompt: int, max_gen: int,
+                  max_arrival: int, min_prompt: int = 1, min_gen: int = 1):
+    """Seeded arrival list for a multi-step serving loop: uid, arrival step ~ U[0,
+    max_arrival], prompt length ~ U[min_prompt, max_prompt], generated tokens ~ U[min_gen,
+    max_gen] (integer uniforms, inclusive), sorted by arrival then uid.  Uids are large,
+    scattered int64 values, so that a ledger cannot rely on small dense keys."""
+    rng = np.random.default_rng(np.random.SeedSequence([20_000, seed]))
+    arrival = rng.integers(0, max_arrival, size=n_requests, endpoint=True)
+    prompt = rng.integers(min_prompt, max_prompt, size=n_requests, endpoint=True)
+    gen = rng.integers(min_gen, max_gen, size=n_requests, endpoint=True)
+    uids = rng.choice(np.arange(1, 1 << 20), size=n_requests, replace=False) * 7919 + \
+        (1 << 40)
+    reqs = [Request(int(u), int(a), int(p), int(g))
+            for u, a, p, g in zip(uids, arrival, prompt, gen)]
+    return sorted(reqs, key=lambda r: (r.arrival, r.uid))
+
+
+def serving_step_qkv(seed: int, step: int, T: int, qkv_heads: int, head_dim: int,
+                     dtype: str):
+    """Fused new rows ``[T][qkv_heads][head_dim]`` of pass ``step`` of a serving loop:
+    N(0, 1) in float32 on the CPU from a generator seeded by (seed, step), stored in
+    ``dtype`` by torch's own cast."""
+    import torch
+
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_torch_seed(np.random.SeedSequence([30_000, seed, step])))
+    x = torch.randn((T, qkv_heads, head_dim), generator=g, dtype=torch.float32)
+    return x.to(_torch_dtype(dtype))
