@@ -232,6 +232,79 @@ def ledger_cost(wl, eng, stream, reps=20):
             "sequences": wl.S, "new_tokens": wl.T, "reps": done}
 
 
+def serving_leg(wl, eng, qkv, pool, out, stream, passes=12, warm=3):
+    """A Dynamic SplitFuse serving loop on the bench's shapes, end to end per pass:
+    compose the batch on the native ledger (the decodes of the batch's single-token
+    sequences first, then a seeded queue of prompts of 256..4096 tokens cut to fill the
+    8192-token budget), put, finalize from the ledger, rotary append, attention,
+    synchronize (a serving loop needs the pass's output before composing the next one)
+    and post_forward.  Finished prompts are flushed; decodes run on.  Times are medians
+    over the timed passes."""
+    import torch
+
+    from ragged_blocked_kv_amd.state import SCHED_OK, StateManager
+
+    # The ledger's own token cap only has to admit the history fill below; each pass's
+    # budget is the batch capacity, given to compose.
+    st = StateManager(num_blocks=wl.num_blocks, block_size=wl.block_size,
+                      max_tracked_seqs=4 * wl.max_seqs, max_seqs=wl.max_seqs,
+                      max_tokens=1 << 20, max_context=1 << 30)
+    dec = [i for i in range(wl.S) if wl.n_new[i] == 1]
+    dec_uids = [1_000_000 + i for i in dec]
+    for g in range(0, len(dec), 16):  # cached history of the decoding sequences
+        grp = [(u, int(wl.seen[i])) for u, i in zip(dec_uids[g:g + 16], dec[g:g + 16])
+               if wl.seen[i] > 0]
+        if grp:
+            assert st.put([u for u, _ in grp], [n for _, n in grp]) == SCHED_OK
+            st.post_forward()
+    rng = np.random.default_rng(99)
+    prompts = {}  # uid -> tokens still to feed, in arrival order
+    next_uid = 2_000_000
+    host, gpu, wall, tok = [], [], [], []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k in range(warm + passes):
+        while sum(prompts.values()) < 2 * wl.max_tokens:  # keep the queue full
+            prompts[next_uid] = int(rng.integers(256, 4096, endpoint=True))
+            next_uid += 1
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        queue = dec_uids + list(prompts)
+        pending = [1] * len(dec_uids) + list(prompts.values())
+        uids, n_new = st.compose(queue, pending, wl.max_tokens)
+        assert st.put(uids, n_new) == SCHED_OK
+        b = eng.finalize_state(st, stream=stream)
+        t1 = time.perf_counter()
+        ev0.record(stream)
+        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream, batch=b)
+        eng.attention(qkv, pool, out, stream=stream, batch=b)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        st.post_forward()
+        for u, n in zip(uids.tolist(), n_new.tolist()):
+            if u in prompts:
+                prompts[u] -= n
+                if prompts[u] == 0:
+                    del prompts[u]
+                    st.flush(u)
+        t3 = time.perf_counter()
+        if k >= warm:
+            host.append((t1 - t0 + t3 - t2) * 1e3)
+            gpu.append(ev0.elapsed_time(ev1))
+            wall.append((t3 - t0) * 1e3)
+            tok.append(int(n_new.sum()))
+    return {
+        "tokens_per_s": float(sum(tok) / (sum(wall) * 1e-3)),
+        "ms_per_pass": round(float(np.median(wall)), 3),
+        "host_ms_per_pass": round(float(np.median(host)), 3),
+        "gpu_ms_per_pass": round(float(np.median(gpu)), 3),
+        "tokens_per_pass": int(np.median(tok)),
+        "passes": passes,
+        "batch": f"{len(dec_uids)} decodes + prompts of 256..4096 tokens cut to fill "
+                 f"{wl.max_tokens} tokens",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +400,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
+    # after the timed steps and after the CPU-baseline history has been copied).
+    serving = serving_leg(wl, eng, qkv, pool, out, stream)
+
     phase_ms = {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
                                   for k in range(args.steps)]))
                 for j, p in enumerate(PHASES)}
@@ -387,6 +464,7 @@ def main():
         },
         "finalize_host_and_upload_us": round(finalize_us, 1),
         "ledger": ledger,
+        "splitfuse_serving": serving,
     }
     print(json.dumps(rec), flush=True)
 

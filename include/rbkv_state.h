@@ -151,6 +151,30 @@ rbkv_status rbkv_state_query(const rbkv_state* s, int64_t uid, int32_t max_new_t
 rbkv_status rbkv_state_can_schedule(const rbkv_state* s, int32_t n, const int64_t* uids,
                                     const int32_t* n_new, int32_t* verdict);
 
+/* Dynamic SplitFuse composition of the next batch from a queue of candidates, without
+ * changing anything.  Candidate i is sequence uids[i] (tracked or new) with pending[i]
+ * tokens waiting to be fed: 1 for a decode, the rest of its prompt for a prefill.  The
+ * batch mixes single-token decodes and prefill chunks in one pass and fills the token
+ * budget by cutting a prompt that does not fit into a chunk of what is left; the rest of
+ * that prompt waits for later passes ("DeepSpeed-Inference and DeepSpeed-MII",
+ * sections 10.3 and 10.10: prefill and decode requests of the queue are merged into one
+ * forward pass before put).  Rule, with budget = min(token_budget, max_tokens):
+ *   two walks over the queue in its order, first the candidates with pending = 1, then
+ *   those with pending > 1; each candidate, while fewer than max_seqs are chosen and
+ *   budget is left, is offered want = min(pending, budget left, max_context - cached)
+ *   tokens, cut further to what the free blocks not yet promised can hold (the
+ *   rbkv_state_query rule with max_new_blocks = those blocks); a new uid needs a free
+ *   tracked slot.  A candidate offered nothing is skipped.  The chosen (uid, tokens)
+ *   pairs are written in choice order (decodes first) to out_uids / out_n, which must
+ *   hold min(n, max_seqs) entries; *S receives their count.  rbkv_state_put of that
+ *   list returns RBKV_SCHED_OK.  While a batch is open its in-flight tokens count as
+ *   cached.
+ * Errors: INVALID_ARG (NULL, n < 0, token_budget < 1, pending[i] < 1, a uid listed
+ * twice), CAPACITY (n > 65536). */
+rbkv_status rbkv_state_compose(const rbkv_state* s, int32_t n, const int64_t* uids,
+                               const int32_t* pending, int32_t token_budget, int32_t* S,
+                               int64_t* out_uids, int32_t* out_n);
+
 /* Open a batch: if can_schedule's verdict is OK, create the new sequences, extend each
  * sequence's block list to cover its cached + new tokens (blocks from the allocator) and
  * record n_new as in flight; otherwise change nothing.  *verdict receives the verdict

@@ -23,6 +23,11 @@ Parity status per function (what pins each one, in ``tests/test_oracle_pins.py``
                                            ragged = alone, block permutation / size
                                            invariance; the GQA head map h // G is a
                                            reading (parity unpinned beyond Hq = Hkv)
+* ``state_manager`` (allocator, ledger,  -- pinned: hand-derived walk
+  compose, kv_requirements, ServingLoop)   (``tests/golden/ledger_walk.txt``), token-by-token
+                                           block-growth simulation, conservation invariants,
+                                           compose properties through can_schedule, loop =
+                                           blocked oracle on one pass, chunking invariance
 """
 from .ragged_attention import (  # noqa: F401
     bf16_to_f64,

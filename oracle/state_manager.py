@@ -178,6 +178,55 @@ class StateManager:
                 return "kv_limit"
         return "ok"
 
+    def compose(self, uids, pending, token_budget):
+        """Dynamic SplitFuse: the next batch [(uid, tokens)] from a queue of candidates
+        (uid, pending tokens), mixing decodes and prefill chunks and cutting a prompt
+        that does not fit into a chunk of what is left.
+
+        Steps (the reading of the pages' idea; nothing here is changed):
+        1. budget = min(token_budget, max_tokens); the free blocks and tracked slots
+           not yet promised start at the ledger's counts;
+        2. walk the queue in order taking only single-token candidates (decodes), then
+           walk it again taking the longer ones (prefills);
+        3. stop a walk when max_seqs candidates are chosen or the budget is spent;
+        4. a new uid needs an unpromised tracked slot, else it is skipped;
+        5. offer min(pending, budget left, max_context - cached) tokens and cut the offer
+           to what the unpromised free blocks can hold (``kv_requirements``); skip the
+           candidate if nothing is left, else choose it and promise its tokens, blocks
+           and (if new) its slot.
+        """
+        uids, pending = [int(u) for u in uids], [int(p) for p in pending]
+        if int(token_budget) < 1 or any(p < 1 for p in pending):
+            raise ValueError("bad budget or pending count")
+        if len(set(uids)) != len(uids):
+            raise ValueError("uid listed twice")
+        left = min(int(token_budget), self.max_tokens)
+        free_left = self.free_blocks
+        tracked = self.n_tracked
+        chosen = []
+        for decodes in (True, False):
+            for u, p in zip(uids, pending):
+                if len(chosen) == self.max_seqs or left == 0:
+                    break
+                if (p == 1) != decodes:
+                    continue
+                is_new = u not in self.seqs
+                if is_new and tracked >= self.max_tracked_seqs:
+                    continue
+                cached, held = self._cached_and_held(u)
+                want = min(p, left, self.max_context - cached)
+                if want <= 0:
+                    continue
+                tokens, blocks = kv_requirements(cached, held, want, free_left,
+                                                 self.block_size)
+                if tokens == 0:
+                    continue
+                chosen.append((u, tokens))
+                left -= tokens
+                free_left -= blocks
+                tracked += is_new
+        return chosen
+
     # -- mutations ----------------------------------------------------------------
     def put(self, uids, n_new) -> str:
         if self.open is not None:

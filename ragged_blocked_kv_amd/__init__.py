@@ -54,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "rbkv_state_block_ids",
     "rbkv_state_query",
     "rbkv_state_can_schedule",
+    "rbkv_state_compose",
     "rbkv_state_put",
     "rbkv_state_batch",
     "rbkv_state_finalize",

@@ -165,6 +165,45 @@ struct rbkv_state {
 
   int32_t n_tracked() const { return cfg.max_tracked_seqs - (int32_t)free_slots.size(); }
 
+  // Cached (seen + in-flight) and held blocks of the sequence in `slot` (-1: new).
+  void cached_held(int32_t slot, int64_t* cached, int64_t* held) const {
+    if (slot < 0) {
+      *cached = 0;
+      *held = 0;
+    } else {
+      const Seq& q = slots[(size_t)slot];
+      *cached = (int64_t)q.seen + q.in_flight;
+      *held = (int64_t)q.blocks.size();
+    }
+  }
+
+  // Look up n (<= kMaxBatchSeqs) uids into looked_up[0..n-1]; false if one is listed
+  // twice or a count is below 1.
+  bool lookup(int32_t n, const int64_t* uids, const int32_t* counts) {
+    if (++stamp == 0) {
+      std::fill(slot_stamp.begin(), slot_stamp.end(), 0u);
+      stamp = 1;
+    }
+    new_uids.clear();
+    for (int32_t i = 0; i < n; ++i) {
+      if (counts[i] < 1) return false;
+      const int32_t slot = index.find(uids[i]);
+      looked_up[(size_t)i] = slot;
+      if (slot >= 0) {
+        if (slot_stamp[(size_t)slot] == stamp) return false;  // listed twice
+        slot_stamp[(size_t)slot] = stamp;
+      } else {
+        new_uids.push_back(uids[i]);  // capacity kMaxBatchSeqs: no allocation
+      }
+    }
+    if (new_uids.size() > 1) {
+      std::sort(new_uids.begin(), new_uids.end());
+      if (std::adjacent_find(new_uids.begin(), new_uids.end()) != new_uids.end())
+        return false;
+    }
+    return true;
+  }
+
   // Validation and verdict shared by can_schedule and put.  Fills looked_up[0..n-1].
   rbkv_status evaluate(int32_t n, const int64_t* uids, const int32_t* n_new, int32_t* verdict) {
     if (n < 0 || !verdict) return RBKV_ERR_INVALID_ARG;
@@ -175,29 +214,9 @@ struct rbkv_state {
       *verdict = RBKV_SCHED_BATCH_SEQ_LIMIT;
       return RBKV_OK;
     }
-    if (++stamp == 0) {
-      std::fill(slot_stamp.begin(), slot_stamp.end(), 0u);
-      stamp = 1;
-    }
-    new_uids.clear();
+    if (!lookup(n, uids, n_new)) return RBKV_ERR_INVALID_ARG;
     int64_t tokens = 0;
-    for (int32_t i = 0; i < n; ++i) {
-      if (n_new[i] < 1) return RBKV_ERR_INVALID_ARG;
-      tokens += n_new[i];
-      const int32_t slot = index.find(uids[i]);
-      looked_up[(size_t)i] = slot;
-      if (slot >= 0) {
-        if (slot_stamp[(size_t)slot] == stamp) return RBKV_ERR_INVALID_ARG;  // listed twice
-        slot_stamp[(size_t)slot] = stamp;
-      } else {
-        new_uids.push_back(uids[i]);  // capacity kMaxBatchSeqs: no allocation
-      }
-    }
-    if (new_uids.size() > 1) {
-      std::sort(new_uids.begin(), new_uids.end());
-      if (std::adjacent_find(new_uids.begin(), new_uids.end()) != new_uids.end())
-        return RBKV_ERR_INVALID_ARG;
-    }
+    for (int32_t i = 0; i < n; ++i) tokens += n_new[i];
     if (n > cfg.max_seqs) {
       *verdict = RBKV_SCHED_BATCH_SEQ_LIMIT;
       return RBKV_OK;
@@ -210,16 +229,11 @@ struct rbkv_state {
     const int64_t free_blocks = alloc.n_free();
     for (int32_t i = 0; i < n; ++i) {
       const int32_t slot = looked_up[(size_t)i];
-      int64_t cached = 0, held = 0;
-      if (slot < 0) {
-        if (++tracked > cfg.max_tracked_seqs) {
-          *verdict = RBKV_SCHED_ENGINE_SEQ_LIMIT;
-          return RBKV_OK;
-        }
-      } else {
-        const Seq& q = slots[(size_t)slot];
-        cached = (int64_t)q.seen + q.in_flight;
-        held = (int64_t)q.blocks.size();
+      int64_t cached, held;
+      cached_held(slot, &cached, &held);
+      if (slot < 0 && ++tracked > cfg.max_tracked_seqs) {
+        *verdict = RBKV_SCHED_ENGINE_SEQ_LIMIT;
+        return RBKV_OK;
       }
       const int64_t total = cached + n_new[i];
       if (total > cfg.max_context) {
@@ -375,6 +389,48 @@ rbkv_status rbkv_state_query(const rbkv_state* s, int64_t uid, int32_t max_new_t
     *tokens = (int32_t)((held + max_new_blocks) * bs - cached);
     *blocks = max_new_blocks;
   }
+  return RBKV_OK;
+}
+
+rbkv_status rbkv_state_compose(const rbkv_state* s, int32_t n, const int64_t* uids,
+                               const int32_t* pending, int32_t token_budget, int32_t* S,
+                               int64_t* out_uids, int32_t* out_n) {
+  if (!s || !S || n < 0 || token_budget < 1) return RBKV_ERR_INVALID_ARG;
+  if (n > 0 && (!uids || !pending || !out_uids || !out_n)) return RBKV_ERR_INVALID_ARG;
+  if (n > kMaxBatchSeqs) return RBKV_ERR_CAPACITY;
+  // Only scratch members change; the ledger itself is untouched.
+  rbkv_state* m = const_cast<rbkv_state*>(s);
+  if (!m->lookup(n, uids, pending)) return RBKV_ERR_INVALID_ARG;
+  const rbkv_state_config& c = s->cfg;
+  const int64_t bs = c.block_size;
+  int64_t left = std::min(token_budget, c.max_tokens);
+  int64_t free_left = s->alloc.n_free();
+  int64_t tracked = s->n_tracked();
+  int32_t count = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int32_t i = 0; i < n && count < c.max_seqs && left > 0; ++i) {
+      if ((pending[i] == 1) != (pass == 0)) continue;
+      const int32_t slot = m->looked_up[(size_t)i];
+      if (slot < 0 && tracked >= c.max_tracked_seqs) continue;
+      int64_t cached, held;
+      s->cached_held(slot, &cached, &held);
+      const int64_t want = std::min<int64_t>({(int64_t)pending[i], left, c.max_context - cached});
+      if (want <= 0) continue;
+      int64_t tokens = want, blocks = std::max<int64_t>(0, cdiv(cached + want, bs) - held);
+      if (blocks > free_left) {  // cut to what the unpromised free blocks can hold
+        tokens = (held + free_left) * bs - cached;
+        blocks = free_left;
+      }
+      if (tokens <= 0) continue;
+      out_uids[count] = uids[i];
+      out_n[count] = (int32_t)tokens;
+      ++count;
+      left -= tokens;
+      free_left -= blocks;
+      if (slot < 0) ++tracked;
+    }
+  }
+  *S = count;
   return RBKV_OK;
 }
 

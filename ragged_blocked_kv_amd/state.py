@@ -62,6 +62,7 @@ def _lib():
             "rbkv_state_block_ids": [vp, ctypes.c_int64, _PI32, _I32, _PI32],
             "rbkv_state_query": [vp, ctypes.c_int64, _I32, _I32, _PI32, _PI32],
             "rbkv_state_can_schedule": [vp, _I32, _PI64, _PI32, _PI32],
+            "rbkv_state_compose": [vp, _I32, _PI64, _PI32, _I32, _PI32, _PI64, _PI32],
             "rbkv_state_put": [vp, _I32, _PI64, _PI32, _PI32],
             "rbkv_state_batch": [vp, _PI32, ctypes.POINTER(_PI32), ctypes.POINTER(_PI32),
                                  ctypes.POINTER(ctypes.POINTER(_PI32)), ctypes.POINTER(_PI32)],
@@ -202,6 +203,24 @@ class StateManager:
         st, v = self.can_schedule_status(uids, n_new)
         check(st, "rbkv_state_can_schedule")
         return v
+
+    def compose_status(self, uids: Sequence[int], pending: Sequence[int], token_budget: int):
+        """(status, uids, n): the Dynamic SplitFuse batch for a queue of candidates."""
+        u, p = _i64(uids), _i32(pending)
+        cap = max(1, min(int(u.size), int(self.config.max_seqs)))
+        out_u = np.zeros(cap, dtype=np.int64)
+        out_n = np.zeros(cap, dtype=np.int32)
+        S = ctypes.c_int32(0)
+        st = _lib().rbkv_state_compose(self._h, int(u.size), u.ctypes.data_as(_PI64),
+                                       p.ctypes.data_as(_PI32), int(token_budget),
+                                       ctypes.byref(S), out_u.ctypes.data_as(_PI64),
+                                       out_n.ctypes.data_as(_PI32))
+        return st, out_u[:S.value].copy(), out_n[:S.value].copy()
+
+    def compose(self, uids, pending, token_budget):
+        st, u, n = self.compose_status(uids, pending, token_budget)
+        check(st, "rbkv_state_compose")
+        return u, n
 
     # -- mutations -----------------------------------------------------------------
     def put_status(self, uids: Sequence[int], n_new: Sequence[int]):

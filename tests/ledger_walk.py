@@ -45,6 +45,10 @@ class OracleSide:
         st, r = self._call(lambda: L.put(uids, n))
         return r if st == "ok" else st
 
+    def compose(self, L, budget, uids, pending):
+        st, r = self._call(lambda: L.compose(uids, pending, budget))
+        return [(int(u), int(n)) for u, n in r] if st == "ok" else st
+
     def batch(self, L):
         st, r = self._call(lambda: L.batch())
         if st != "ok":
@@ -101,6 +105,12 @@ class NativeSide:
     def put(self, L, uids, n):
         st, v = L.put_status(uids, n)
         return VERDICT_NAMES[v] if st == self.R.OK else self._status(st)
+
+    def compose(self, L, budget, uids, pending):
+        st, u, n = L.compose_status(uids, pending, budget)
+        if st != self.R.OK:
+            return self._status(st)
+        return [(int(a), int(b)) for a, b in zip(u, n)]
 
     def batch(self, L):
         try:
@@ -174,6 +184,11 @@ def run(side, path=GOLDEN):
             uids, n = _pairs(args)
             got = getattr(side, op)(L, uids, n)
             ok = [got] == expect
+        elif op == "compose":
+            uids, n = _pairs(args[1:])
+            got = side.compose(L, int(args[0]), uids, n)
+            ok = (expect == ["invalid"] and got == "invalid") or \
+                (got != "invalid" and got == [tuple(int(x) for x in e.split(":")) for e in expect])
         elif op == "batch":
             got = side.batch(L)
             want = [tuple(int(x) for x in e.split("/")) for e in expect]

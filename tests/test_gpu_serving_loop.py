@@ -198,3 +198,118 @@ def test_serving_loop_matches_oracle(case):
     # the loop exercised what it is for
     assert stats["kv_limit"] > 0, "pool never ran short"
     assert any(len(s) > 1 for s in owners.values()), "no block was reused"
+
+
+SPLITFUSE_CASES = [
+    # prompts up to 3x the token budget: every long prompt is fed in chunks
+    Case("sf_bf16_g4_bs16", "bf16", 8, 2, 128, 16, 30, 6, 6, 64, 12, 190, 20, 10, 3),
+    Case("sf_f32_g2_bs32", "f32", 4, 2, 64, 32, 14, 5, 5, 48, 10, 140, 16, 8, 4),
+    Case("sf_bf16_g8_bs64", "bf16", 16, 2, 64, 64, 10, 4, 4, 100, 8, 300, 40, 6, 5),
+]
+
+
+@pytest.mark.parametrize("case", SPLITFUSE_CASES, ids=lambda c: c.name)
+def test_splitfuse_loop_matches_oracle(case):
+    """The same loop with batches composed by Dynamic SplitFuse on both ledgers (the
+    composed batches must be identical): decodes first, then prompts in arrival order
+    cut to fill the token budget, the rest of a prompt continuing in later passes."""
+    from ragged_blocked_kv_amd.runtime import Engine
+    from ragged_blocked_kv_amd.state import StateManager
+
+    print(f"splitfuse loop {case.name}", flush=True)
+    dev = torch.device("cuda:0")
+    c = case
+    max_context = c.max_prompt + c.max_gen + 1
+    assert -(-max_context // c.block_size) <= c.num_blocks
+    cfg = dict(num_blocks=c.num_blocks, block_size=c.block_size,
+               max_tracked_seqs=c.max_tracked, max_seqs=c.max_seqs, max_tokens=c.max_tokens,
+               max_context=max_context)
+    nat, ora = StateManager(**cfg), M.StateManager(**cfg)
+    loop = M.ServingLoop(n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim,
+                         rope_base=1e4, dtype=c.dtype)
+    eng = Engine(max_tokens=c.max_tokens, max_seqs=c.max_seqs, num_blocks=c.num_blocks,
+                 block_size=c.block_size, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
+                 head_dim=c.head_dim, dtype=c.dtype, device=dev)
+    pool = torch.zeros((c.num_blocks, 2, c.n_kv_heads, c.block_size, c.head_dim),
+                       dtype=eng.torch_dtype, device=dev)
+    tol = 2e-2 if c.dtype == "bf16" else 1e-4
+
+    trace = W.serving_trace(c.seed, c.n_requests, max_prompt=c.max_prompt,
+                            max_gen=c.max_gen, max_arrival=c.max_arrival)
+    arrival = {r.uid: r.arrival for r in trace}
+    order = [r.uid for r in trace]  # queue order: arrival order, kept across preemption
+    prompt_left = {r.uid: r.prompt for r in trace}
+    dec_left = {r.uid: r.gen for r in trace}
+    fed = {r.uid: 0 for r in trace}  # tokens cached for the sequence
+    done = []
+    stats = dict(passes=0, chunks=0, cut_prompts=0, decodes=0, preempted=0, max_err=0.0)
+
+    def flush_both(u):
+        nat.flush(u)
+        ora.flush(u)
+        loop.flush(u)
+
+    step = 0
+    while order:
+        assert step < 600, "loop did not drain"
+        for u in [u for u in order if prompt_left[u] == 0 and dec_left[u] == 0]:
+            flush_both(u)
+            order.remove(u)
+            done.append(u)
+        queue = [u for u in order if arrival[u] <= step]
+        pending = [prompt_left[u] if prompt_left[u] else 1 for u in queue]
+        while True:
+            got_u, got_n = nat.compose(queue, pending, c.max_tokens)
+            batch = list(zip(got_u.tolist(), got_n.tolist()))
+            assert batch == ora.compose(queue, pending, c.max_tokens), step
+            if batch or not queue:
+                break
+            # nothing fits: flush the youngest tracked sequence, its history becomes prompt
+            tracked = [u for u in order if nat.sequence(u) is not None]
+            assert tracked, "a lone request does not fit an empty pool"
+            u = tracked[-1]
+            flush_both(u)
+            prompt_left[u] += fed[u]
+            fed[u] = 0
+            stats["preempted"] += 1
+            pending = [prompt_left[v] if prompt_left[v] else 1 for v in queue]
+        if not batch:
+            step += 1
+            continue
+        uids, n_new = [u for u, _ in batch], [n for _, n in batch]
+        assert nat.put(uids, n_new) == 0 and ora.put(uids, n_new) == "ok"
+        T = int(sum(n_new))
+        qkv_cpu = W.serving_step_qkv(c.seed, step, T, c.n_q_heads + 2 * c.n_kv_heads,
+                                     c.head_dim, c.dtype)
+        qkv = qkv_cpu.to(dev)
+        out = torch.empty((T, c.n_q_heads, c.head_dim), dtype=eng.torch_dtype, device=dev)
+        eng.finalize_state(nat)
+        eng.append_rotary(qkv, pool, 1e4)
+        eng.attention(qkv, pool, out)
+        torch.cuda.synchronize()
+        want = loop.step(uids, n_new, _storage_numpy(qkv_cpu, c.dtype))
+        err = float(np.max(np.abs(out.float().cpu().numpy().astype(np.float64) - want)))
+        assert err <= tol, (step, batch, err)
+        stats["max_err"] = max(stats["max_err"], err)
+        nat.post_forward()
+        ora.post_forward()
+        for u, n in batch:
+            fed[u] += n
+            if prompt_left[u]:
+                stats["chunks"] += 1
+                stats["cut_prompts"] += n < prompt_left[u]
+                prompt_left[u] -= n
+            else:
+                dec_left[u] -= 1
+                stats["decodes"] += 1
+        assert nat.counts() == (ora.free_blocks, ora.n_tracked)
+        for u in uids:
+            assert nat.sequence(u) == ora.sequence(u) == (fed[u], 0, -(-fed[u] // c.block_size))
+            assert loop.seen(u) == fed[u]
+        stats["passes"] += 1
+        step += 1
+
+    print(f"  {case.name}: {stats}", flush=True)
+    assert sorted(done) == sorted(r.uid for r in trace)
+    assert nat.counts() == (c.num_blocks, 0)
+    assert stats["cut_prompts"] > 0, "no prompt was split across passes"

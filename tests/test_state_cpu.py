@@ -201,3 +201,46 @@ def test_batch_views_point_into_the_ledger():
     assert nat.put([9, 7], [4, 1]) == S.SCHED_OK  # 9 grows to 5 tokens: a 2nd block
     n_new, seen, lists = nat.batch()
     assert seen.tolist() == [1, 6] and [len(l) for l in lists] == [2, 2]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_compose_matches_oracle(seed):
+    """Dynamic SplitFuse composition is fixed by the ledger's counts alone, so the
+    library's batch must equal the oracle's exactly, through a run of passes in which
+    the composed batch is put, run and closed on both ledgers."""
+    rng = np.random.default_rng(5000 + seed)
+    bs = int(rng.choice([1, 4, 16, 64]))
+    cfg = dict(num_blocks=int(rng.integers(2, 80)), block_size=bs,
+               max_tracked_seqs=int(rng.integers(1, 10)), max_seqs=int(rng.integers(1, 8)),
+               max_tokens=int(rng.integers(1, 200)), max_context=int(rng.integers(1, 400)))
+    ora, nat = M.StateManager(**cfg), S.StateManager(**cfg)
+    uids = [int(u) for u in rng.integers(-(1 << 62), 1 << 62, size=14)]
+    prompt = {u: int(rng.integers(1, 150)) for u in uids}  # prompt tokens not yet fed
+    decode = {u: int(rng.integers(1, 6)) for u in uids}  # decode passes still to run
+    for step in range(120):
+        live = [u for u in rng.permutation(uids).tolist() if prompt[u] or decode[u]]
+        p = [prompt[u] if prompt[u] else 1 for u in live]
+        budget = int(rng.integers(1, 250))
+        want = ora.compose(live, p, budget)
+        u, n = nat.compose(live, p, budget)
+        assert list(zip(u.tolist(), n.tolist())) == want, step
+        if want:
+            assert nat.put(u, n) == S.SCHED_OK and ora.put(u, n) == "ok"
+            nat.post_forward()
+            ora.post_forward()
+            for a, b in want:
+                if prompt[a]:
+                    prompt[a] -= b
+                else:
+                    decode[a] -= 1
+        for a in uids:  # finished: flush, and a new request arrives on the same uid
+            if not prompt[a] and not decode[a]:
+                nat.flush(a)
+                ora.flush(a)
+                prompt[a], decode[a] = int(rng.integers(1, 150)), int(rng.integers(1, 6))
+        assert nat.counts() == (ora.free_blocks, ora.n_tracked)
+    # compose argument errors
+    assert nat.compose_status([1, 1], [1, 1], 5)[0] == R.ERR_INVALID_ARG
+    assert nat.compose_status([1], [0], 5)[0] == R.ERR_INVALID_ARG
+    assert nat.compose_status([1], [1], 0)[0] == R.ERR_INVALID_ARG
+    assert nat.compose_status([], [], 5)[0] == R.OK

@@ -112,11 +112,6 @@ def test_ledger_invariants_under_random_operations(seed):
     assert "ok" in verdicts
 
 
-def _bf16(x):
-    import torch
-    return x.to(torch.bfloat16)
-
-
 def test_serving_loop_matches_blocked_oracle_on_one_pass():
     """One mixed pass of the loop equals the pinned blocked-pool oracle on the same batch
     (empty history, fresh sequences, blocks laid out in batch order)."""
@@ -159,3 +154,74 @@ def test_serving_loop_is_chunking_invariant():
     assert parts.seen(1) == 23
     parts.flush(1)
     assert parts.seen(1) == 0
+
+
+def _random_ledger(rng):
+    bs = int(rng.choice([1, 4, 16]))
+    cfg = dict(num_blocks=int(rng.integers(4, 60)), block_size=bs,
+               max_tracked_seqs=int(rng.integers(1, 8)), max_seqs=int(rng.integers(1, 6)),
+               max_tokens=int(rng.integers(1, 80)), max_context=int(rng.integers(1, 120)))
+    L = M.StateManager(**cfg)
+    uids = list(range(1, 11))
+    for _ in range(int(rng.integers(0, 30))):  # random history
+        if rng.random() < 0.7:
+            us = [int(u) for u in rng.choice(uids, size=int(rng.integers(1, 4)), replace=False)]
+            L.put(us, [int(rng.integers(1, 30)) for _ in us])
+            if L.open is not None:
+                L.post_forward()
+        else:
+            u = int(rng.choice(uids))
+            if u in L.seqs:
+                L.flush(u)
+    return L, uids
+
+
+def _fits(L, batch, budget):
+    if not batch:
+        return True
+    if len(batch) > L.max_seqs or sum(n for _, n in batch) > min(budget, L.max_tokens):
+        return False
+    return L.can_schedule([u for u, _ in batch], [n for _, n in batch]) == "ok"
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_compose_is_schedulable_maximal_and_decodes_first(seed):
+    """What Dynamic SplitFuse promises, checked through can_schedule rather than by
+    re-running the greedy: the composed batch can be put; no candidate can take one
+    more token without breaking a limit (the budget is filled as far as the limits
+    allow); and a decode is left out only if it would not fit even beside the chosen
+    decodes alone (prefill chunks never displace decodes)."""
+    rng = np.random.default_rng(seed)
+    L, uids = _random_ledger(rng)
+    queue = [int(u) for u in rng.permutation(uids)[:int(rng.integers(0, 10))]]
+    pending = [1 if rng.random() < 0.4 else int(rng.integers(2, 50)) for _ in queue]
+    budget = int(rng.integers(1, 100))
+    batch = L.compose(queue, pending, budget)
+    assert _fits(L, batch, budget)
+    got = dict(batch)
+    # chosen in two walks: decodes first, each walk in queue order
+    order = [u for u, p in zip(queue, pending) if p == 1] + \
+        [u for u, p in zip(queue, pending) if p > 1]
+    assert [u for u, _ in batch] == [u for u in order if u in got]
+    for u, p in zip(queue, pending):
+        assert got.get(u, 0) <= p
+        if got.get(u, 0) < p:  # one more token for u must break a limit
+            more = [(v, n + (v == u)) for v, n in batch] + ([] if u in got else [(u, 1)])
+            assert not _fits(L, more, budget), (u, batch)
+    decodes = [(u, got[u]) for u, p in zip(queue, pending) if p == 1 and u in got]
+    for u, p in zip(queue, pending):
+        if p == 1 and u not in got:
+            assert not _fits(L, decodes + [(u, 1)], budget), (u, batch)
+    if L.open is None and batch:
+        assert L.put([u for u, _ in batch], [n for _, n in batch]) == "ok"
+
+
+def test_compose_fills_the_budget_when_nothing_else_binds():
+    L = M.StateManager(num_blocks=1000, block_size=16, max_tracked_seqs=64, max_seqs=64,
+                       max_tokens=512, max_context=4096)
+    queue = list(range(100, 140))
+    pending = [1] * 20 + [300, 7, 250, 90] + [1000] * 16
+    batch = L.compose(queue, pending, 512)
+    assert sum(n for _, n in batch) == 512
+    assert [n for _, n in batch[:20]] == [1] * 20
+    assert batch[20:] == [(120, 300), (121, 7), (122, 185)]  # the third prompt is cut
