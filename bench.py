@@ -57,27 +57,32 @@ def kernel_source_digest(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_file, workload):
+def measured_traffic(label, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
-    the current source of that kernel (else None)."""
+    the current source of that kernel group (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        rec = json.load(open(p)).get(f"{kernel_file}:{workload}")
+        rec = json.load(open(p)).get(f"{label}:{workload}")
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_sha") != kernel_source_digest(kernel_file):
+    if not rec or rec.get("source_sha") != kernel_source_digest(KERNEL_GROUPS[label][0]):
         return None
     return rec.get("bytes_per_launch")  # bytes per launch (fetch + write), scaled
 
 
-# Library kernels by source file (a file may hold several kernels).
-KERNEL_FILES = {"attn_prefill.hip": ("prefill_attn_kernel",),
-                "attn_decode.hip": ("decode_attn_kernel", "decode_group_kernel"),
-                "append_rotary.hip": ("append_rotary_kernel",),
-                "attn_combine.hip": ("combine_kernel",),
-                "meta_build.hip": ("meta_build_kernel",)}
+# Library kernels in groups for the HBM-traffic reduction: label -> (source file, kernel
+# name fragments).  A label's record is valid while its source file hashes the same.
+KERNEL_GROUPS = {
+    "attn_prefill.hip": ("attn_prefill.hip", ("prefill_attn_kernel",)),
+    "attn_decode.hip": ("attn_decode.hip", ("decode_attn_kernel", "decode_group_kernel")),
+    "append_rotary.hip": ("append_rotary.hip", ("append_rotary_kernel",)),
+    "attn_combine.hip": ("attn_combine.hip", ("combine_kernel",)),
+    "meta_build.hip": ("meta_build.hip", ("meta_build_kernel",)),
+    "gather.hip/embedding": ("gather.hip", ("embedding_gather_kernel",)),
+    "gather.hip/logits": ("gather.hip", ("logits_gather_kernel",)),
+}
 
 
 def decode_kernel_name(wl):
@@ -121,7 +126,7 @@ def traffic_from_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, ca
     f_scale = cal_bytes / (big(cf) * 1024.0)
     w_scale = cal_bytes / (big(cw) * 1024.0)
     rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
-    for kfile, knames in KERNEL_FILES.items():
+    for label, (kfile, knames) in KERNEL_GROUPS.items():
         sel = lambda n, ks=knames: any(k in n for k in ks)
         fv = list(_counter_per_dispatch(fetch_csv, "FETCH_SIZE", sel).values())
         wv = list(_counter_per_dispatch(write_csv, "WRITE_SIZE", sel).values())
@@ -129,7 +134,7 @@ def traffic_from_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, ca
             continue
         fb = float(np.mean(fv)) * 1024.0 * f_scale
         wb = float(np.mean(wv)) * 1024.0 * w_scale
-        rec[f"{kfile}:{workload}"] = {
+        rec[f"{label}:{workload}"] = {
             "source_sha": kernel_source_digest(kfile),
             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
             "bytes_per_launch": fb + wb, "dispatches": len(fv),
@@ -305,6 +310,57 @@ def serving_leg(wl, eng, qkv, pool, out, stream, passes=12, warm=3):
     }
 
 
+def gathers_leg(wl, eng, stream, reps=20, warm=3):
+    """The two row gathers around the layer stack on the bench batch, at Llama-2-7B widths
+    (the model the pages' install example loads): embedding rows (hidden 4096) of the
+    8192 packed tokens from a 32000-row table, and the last-token rows of the 256
+    sequences from vocabulary-wide (32000) logits of every token.  Average microseconds
+    per launch from HIP events on the stream; algorithmic bytes are the rows read and
+    written plus the index words."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    vocab, hidden = 32000, 4096
+    g = torch.Generator(device=dev).manual_seed(7)
+    table = torch.randn((vocab, hidden), generator=g, device=dev).to(torch.bfloat16)
+    ids = torch.randint(0, vocab, (wl.T,), generator=g, device=dev, dtype=torch.int32)
+    emb = torch.empty((wl.T, hidden), dtype=torch.bfloat16, device=dev)
+    logits = torch.randn((wl.T, vocab), generator=g, device=dev).to(torch.bfloat16)
+    last = torch.empty((wl.S, vocab), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for name, fn, nbytes in (
+            ("embedding", lambda: eng.embedding_gather(ids, table, emb, stream=stream),
+             2 * wl.T * hidden * 2 + 4 * wl.T),
+            ("logits", lambda: eng.logits_gather(logits, last, stream=stream),
+             2 * wl.S * vocab * 2 + 4 * (wl.S + 1))):
+        for _ in range(warm):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"kernel": f"{name}_gather_kernel", "us": round(us, 2), "bytes": nbytes,
+                     "GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"gather.hip/{name}", wl.name)}
+    # Context: what a plain 1 GiB device copy (read + write) reaches on this part.
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    big2.copy_(big)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        big2.copy_(big)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["copy_1GiB_GBs"] = round(2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    res["widths"] = f"hidden {hidden}, vocab {vocab}, bf16"
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +369,11 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    # The extra legs launch library kernels on other batches; profiles of the main step
+    # switch them off so that per-kernel averages cover the bench batch only.
+    ap.add_argument("--no-ledger", action="store_true", help="skip the ledger host-cost leg")
+    ap.add_argument("--no-serving", action="store_true", help="skip the SplitFuse serving leg")
+    ap.add_argument("--no-gathers", action="store_true", help="skip the row-gather leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=5, default=None,
@@ -359,9 +420,11 @@ def main():
 
     # Native ledger around the same batch (host only; its finalize rewrites the device
     # metadata, so the bench batch is finalized again afterwards).
-    ledger = ledger_cost(wl, eng, stream)
-    eng.finalize(wl.n_new, wl.seen, wl.block_lists, stream=stream)
-    torch.cuda.synchronize()
+    ledger = None
+    if not args.no_ledger:
+        ledger = ledger_cost(wl, eng, stream)
+        eng.finalize(wl.n_new, wl.seen, wl.block_lists, stream=stream)
+        torch.cuda.synchronize()
 
     # CPU-baseline inputs: the pool history of the sampled sequences, copied before the
     # first append overwrites this pass's slots.
@@ -402,7 +465,8 @@ def main():
 
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
-    serving = serving_leg(wl, eng, qkv, pool, out, stream)
+    gathers = None if args.no_gathers else gathers_leg(wl, eng, stream)
+    serving = None if args.no_serving else serving_leg(wl, eng, qkv, pool, out, stream)
 
     phase_ms = {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
                                   for k in range(args.steps)]))
@@ -465,6 +529,7 @@ def main():
         "finalize_host_and_upload_us": round(finalize_us, 1),
         "ledger": ledger,
         "splitfuse_serving": serving,
+        "gathers": gathers,
     }
     print(json.dumps(rec), flush=True)
 

@@ -226,6 +226,29 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
                                            void* out, void* workspace, size_t workspace_bytes,
                                            void* stream);
 
+/* The two row gathers that frame the layer stack over the same ragged batch ("DeepSpeed
+ * Inference v2 source tour", section "Ragged batches: packing a whole server into four
+ * tensors": the ragged embedding kernel gathers embedding rows for the packed token
+ * stream, and the logits gather copies out only each sequence's last-token row for
+ * sampling).  Both copy whole rows byte for byte; `dtype` (RBKV_DTYPE_*) only sets the
+ * element size.  A row must be a multiple of 16 bytes and every buffer 16-byte aligned.
+ * `batch` is a finalized batch (its T, S and device cu_seqlens are used); no shape is
+ * needed.  Errors: INVALID_ARG (NULL, width or vocab < 1, bad dtype, misaligned buffer,
+ * a batch outside its shape's limits), UNSUPPORTED (row bytes not a multiple of 16, or
+ * more than 2^31 16-byte words to copy), DEVICE_PTR, HIP. */
+
+/* out[t][:] = table[token_ids[t]][:] for t < batch->T.  token_ids: device int32 [T];
+ * table: device [vocab][width]; out: device [T][width].  An id outside [0, vocab) gives a
+ * zero row (device ids cannot be checked on the host without a synchronisation). */
+rbkv_status ragged_embedding_gather(const rbkv_batch* batch, const int32_t* token_ids,
+                                    const void* table, int32_t vocab, int32_t width,
+                                    int32_t dtype, void* out, void* stream);
+
+/* out[i][:] = rows[cu_seqlens[i + 1] - 1][:] for i < batch->S: the row of each
+ * sequence's last new token.  rows: device [T][width]; out: device [S][width]. */
+rbkv_status ragged_logits_gather(const rbkv_batch* batch, const void* rows, int32_t width,
+                                 int32_t dtype, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

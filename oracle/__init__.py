@@ -23,6 +23,8 @@ Parity status per function (what pins each one, in ``tests/test_oracle_pins.py``
                                            ragged = alone, block permutation / size
                                            invariance; the GQA head map h // G is a
                                            reading (parity unpinned beyond Hq = Hkv)
+* ``embedding_gather`` / ``logits_gather`` -- pinned: hand fixture, last token derived
+                                           from token_to_seq
 * ``state_manager`` (allocator, ledger,  -- pinned: hand-derived walk
   compose, kv_requirements, ServingLoop)   (``tests/golden/ledger_walk.txt``), token-by-token
                                            block-growth simulation, conservation invariants,
@@ -43,3 +45,4 @@ from .ragged_attention import (  # noqa: F401
     sequence_attention,
     ragged_attention,
 )
+from .gather import embedding_gather, logits_gather  # noqa: F401

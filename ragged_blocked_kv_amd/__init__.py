@@ -19,7 +19,8 @@ __all__ = [
     "RbkvError", "Shape", "Batch", "lib", "status_string", "check",
     "rbkv_metadata_bytes", "rbkv_workspace_bytes", "ragged_batch_finalize",
     "blocked_kv_append_rotary", "ragged_blocked_attention", "ragged_batch_rebuild",
-    "ragged_blocked_attention_phase", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
+    "ragged_blocked_attention_phase", "ragged_embedding_gather", "ragged_logits_gather",
+    "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
     "PHASE_DECODE", "PHASE_COMBINE",
     "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
     "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "ERR_HOST_MEMORY", "DTYPE_F32", "DTYPE_BF16",
@@ -41,6 +42,8 @@ EXPORTED_SYMBOLS = (
     "blocked_kv_append_rotary",
     "ragged_blocked_attention",
     "ragged_blocked_attention_phase",
+    "ragged_embedding_gather",
+    "ragged_logits_gather",
     # include/rbkv_state.h (bound in ragged_blocked_kv_amd.state)
     "rbkv_allocator_create",
     "rbkv_allocator_destroy",
@@ -129,6 +132,14 @@ def lib():
         L.blocked_kv_append_rotary.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_double, ctypes.c_void_p]
+        L.ragged_embedding_gather.restype = ctypes.c_int32
+        L.ragged_embedding_gather.argtypes = [
+            ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        L.ragged_logits_gather.restype = ctypes.c_int32
+        L.ragged_logits_gather.argtypes = [
+            ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p]
         L.ragged_blocked_attention.restype = ctypes.c_int32
         L.ragged_blocked_attention.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
@@ -227,3 +238,19 @@ def ragged_blocked_attention_phase(shape: Shape, batch: Batch, phase: int, qkv, 
     return lib().ragged_blocked_attention_phase(
         ctypes.byref(shape), ctypes.byref(batch), int(phase), _ptr(qkv), _ptr(kv_pool),
         _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def _dtype_code(dtype) -> int:
+    return {"f32": DTYPE_F32, "bf16": DTYPE_BF16}.get(dtype, dtype)
+
+
+def ragged_embedding_gather(batch: Batch, token_ids, table, vocab: int, width: int, dtype,
+                            out, stream=None) -> int:
+    return lib().ragged_embedding_gather(ctypes.byref(batch), _ptr(token_ids), _ptr(table),
+                                         int(vocab), int(width), int(_dtype_code(dtype)),
+                                         _ptr(out), _stream(stream))
+
+
+def ragged_logits_gather(batch: Batch, rows, width: int, dtype, out, stream=None) -> int:
+    return lib().ragged_logits_gather(ctypes.byref(batch), _ptr(rows), int(width),
+                                      int(_dtype_code(dtype)), _ptr(out), _stream(stream))

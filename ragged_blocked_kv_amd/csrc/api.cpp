@@ -366,6 +366,70 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
   return RBKV_OK;
 }
 
+namespace {
+
+// Shared checks of the two gathers; *row_bytes receives width * element size.
+rbkv_status check_gather(const rbkv_batch* batch, int32_t width, int32_t dtype,
+                         int64_t rows, size_t* row_bytes) {
+  if (!batch || width < 1) return RBKV_ERR_INVALID_ARG;
+  if (dtype != RBKV_DTYPE_F32 && dtype != RBKV_DTYPE_BF16) return RBKV_ERR_INVALID_ARG;
+  const rbkv_shape& s = batch->shape;
+  if (batch->T < 0 || batch->T > s.max_tokens || batch->S < 0 || batch->S > s.max_seqs ||
+      batch->S > batch->T)
+    return RBKV_ERR_INVALID_ARG;
+  const size_t rb = (size_t)width * (dtype == RBKV_DTYPE_F32 ? 4 : 2);
+  if (rb % 16 != 0) return RBKV_ERR_UNSUPPORTED;
+  if ((uint64_t)rows * (rb / 16) >= (1ull << 31)) return RBKV_ERR_UNSUPPORTED;
+  *row_bytes = rb;
+  return RBKV_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+rbkv_status ragged_embedding_gather(const rbkv_batch* batch, const int32_t* token_ids,
+                                    const void* table, int32_t vocab, int32_t width,
+                                    int32_t dtype, void* out, void* stream) {
+  size_t rb = 0;
+  rbkv_status st = check_gather(batch, width, dtype, batch ? batch->T : 0, &rb);
+  if (st != RBKV_OK) return st;
+  if (!token_ids || !table || !out || vocab < 1) return RBKV_ERR_INVALID_ARG;
+  if (!aligned16(table) || !aligned16(out)) return RBKV_ERR_INVALID_ARG;
+  const int32_t T = batch->T;
+  if (T == 0) return RBKV_OK;
+  if ((st = check_device(token_ids, (size_t)T * 4)) != RBKV_OK) return st;
+  if ((st = check_device(table, (size_t)vocab * rb)) != RBKV_OK) return st;
+  if ((st = check_device(out, (size_t)T * rb)) != RBKV_OK) return st;
+  if (launch_gather_rows(0, table, out, token_ids, vocab, T, rb, (hipStream_t)stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
+rbkv_status ragged_logits_gather(const rbkv_batch* batch, const void* rows, int32_t width,
+                                 int32_t dtype, void* out, void* stream) {
+  size_t rb = 0;
+  rbkv_status st = check_gather(batch, width, dtype, batch ? batch->S : 0, &rb);
+  if (st != RBKV_OK) return st;
+  if (!rows || !out) return RBKV_ERR_INVALID_ARG;
+  if (!aligned16(rows) || !aligned16(out)) return RBKV_ERR_INVALID_ARG;
+  const int32_t S = batch->S;
+  if (S == 0) return RBKV_OK;
+  if (!batch->cu_seqlens) return RBKV_ERR_INVALID_ARG;
+  if ((st = check_device(batch->cu_seqlens, (size_t)(S + 1) * 4)) != RBKV_OK) return st;
+  if ((st = check_device(rows, (size_t)batch->T * rb)) != RBKV_OK) return st;
+  if ((st = check_device(out, (size_t)S * rb)) != RBKV_OK) return st;
+  if (launch_gather_rows(1, rows, out, batch->cu_seqlens, batch->T, S, rb,
+                         (hipStream_t)stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
 rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
                                      const void* qkv, const void* kv_pool, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream) {

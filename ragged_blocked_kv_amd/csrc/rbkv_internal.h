@@ -139,4 +139,10 @@ hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* 
 hipError_t launch_combine(const rbkv_shape& s, const rbkv_batch& b, const float* ws,
                           void* out, hipStream_t stream);
 
+// Row gather: mode 0 takes source row idx[r] (zero row outside [0, n_src)), mode 1 takes
+// idx[r + 1] - 1.  row_bytes is a multiple of 16; rows * row_bytes / 16 < 2^31.
+hipError_t launch_gather_rows(int mode, const void* src, void* dst, const int32_t* idx,
+                              int32_t n_src, int32_t rows, size_t row_bytes,
+                              hipStream_t stream);
+
 }  // namespace rbkv

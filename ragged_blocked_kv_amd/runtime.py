@@ -9,11 +9,13 @@ from __future__ import annotations
 
 import torch
 
-from . import (Batch, Shape, blocked_kv_append_rotary, check, ragged_batch_finalize,
-               ragged_batch_rebuild, ragged_blocked_attention, ragged_blocked_attention_phase,
+from . import (DTYPE_BF16, DTYPE_F32, Batch, Shape, blocked_kv_append_rotary, check,
+               ragged_batch_finalize, ragged_batch_rebuild, ragged_blocked_attention,
+               ragged_blocked_attention_phase, ragged_embedding_gather, ragged_logits_gather,
                rbkv_metadata_bytes, rbkv_workspace_bytes)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+_DTYPE_CODE = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
 
 
 class Engine:
@@ -102,6 +104,19 @@ class Engine:
         check(ragged_blocked_attention(self.shape, b, qkv, kv_pool, out, self.workspace,
                                        self.workspace.numel(), self.stream(stream)),
               "ragged_blocked_attention")
+
+    def embedding_gather(self, token_ids, table, out, stream=None, batch=None):
+        """out[t] = table[token_ids[t]] for the batch's tokens (ids outside the table give
+        zero rows)."""
+        check(ragged_embedding_gather(batch or self.batch, token_ids, table, table.shape[0],
+                                      table.shape[1], _DTYPE_CODE[table.dtype], out,
+                                      self.stream(stream)), "ragged_embedding_gather")
+
+    def logits_gather(self, rows, out, stream=None, batch=None):
+        """out[i] = rows[last new token of sequence i]."""
+        check(ragged_logits_gather(batch or self.batch, rows, rows.shape[1],
+                                   _DTYPE_CODE[rows.dtype], out, self.stream(stream)),
+              "ragged_logits_gather")
 
     def new_out(self, T=None):
         T = self.batch.T if T is None else T

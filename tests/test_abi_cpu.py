@@ -165,3 +165,39 @@ def test_valid_call_without_gpu_reports_pointer_kind():
     s = shape()
     st, _ = finalize(s, [20, 1], [5, 3], [np.array([0, 1]), np.array([3])])
     assert st in (R.ERR_DEVICE_PTR, R.ERR_HIP)
+
+
+def _fake_batch(S=2, T=5):
+    b = R.Batch()
+    b.shape = shape()
+    b.S, b.T = S, T
+    b.cu_seqlens = FAKE
+    return b
+
+
+def test_gather_validation_errors():
+    b = _fake_batch()
+    emb = lambda **kw: R.ragged_embedding_gather(
+        kw.get("batch", b), kw.get("ids", FAKE), kw.get("table", FAKE), kw.get("vocab", 10),
+        kw.get("width", 64), kw.get("dtype", "bf16"), kw.get("out", FAKE))
+    lg = lambda **kw: R.ragged_logits_gather(
+        kw.get("batch", b), kw.get("rows", FAKE), kw.get("width", 64),
+        kw.get("dtype", "bf16"), kw.get("out", FAKE))
+    for f in (emb, lg):
+        assert f(width=0) == R.ERR_INVALID_ARG
+        assert f(dtype=7) == R.ERR_INVALID_ARG
+        assert f(width=3) == R.ERR_UNSUPPORTED        # 6-byte rows
+        assert f(width=4, dtype="bf16") == R.ERR_UNSUPPORTED
+        # 5 rows of 2^31 - 4 floats: more than 2^31 16-byte words
+        assert f(width=(1 << 31) - 4, dtype="f32", batch=_fake_batch(S=5, T=5)) == \
+            R.ERR_UNSUPPORTED
+        assert f(out=FAKE + 8) == R.ERR_INVALID_ARG   # misaligned
+        assert f(batch=_fake_batch(S=3, T=2)) == R.ERR_INVALID_ARG
+        assert f(batch=_fake_batch(S=2, T=1 << 20)) == R.ERR_INVALID_ARG  # over max_tokens
+    assert emb(vocab=0) == R.ERR_INVALID_ARG
+    assert emb(ids=None) == R.ERR_INVALID_ARG
+    assert emb(table=FAKE + 4) == R.ERR_INVALID_ARG
+    assert lg(rows=None) == R.ERR_INVALID_ARG
+    # empty batches launch nothing and touch no pointer
+    assert emb(batch=_fake_batch(S=0, T=0)) == R.OK
+    assert lg(batch=_fake_batch(S=0, T=0)) == R.OK

@@ -418,3 +418,40 @@ def test_full_workload_oracle_end_to_end_tiny():
     q = q2[37:38, :4]
     want = _bruteforce_attention(q, K, V, 50, 1)
     assert np.max(np.abs(out[37:38] - want)) < 1e-12
+
+
+def test_gathers_hand_fixture():
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "gather_examples.json")))
+    e = fx["embedding"]
+    got = O.embedding_gather(np.array(e["table"], dtype=np.float32), e["token_ids"])
+    assert got.tolist() == e["expect"]
+    lg = fx["logits"]
+    cu = O.batch_metadata(lg["n_new"], [0] * len(lg["n_new"]),
+                          [np.arange(8, dtype=np.int32)] * len(lg["n_new"]), 16)["cu_seqlens"]
+    got = O.logits_gather(np.array(lg["rows"], dtype=np.float32), cu)
+    assert got.tolist() == lg["expect"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_logits_gather_is_the_last_token_of_each_sequence(seed):
+    """The last-token row found another way: scan token_to_seq for the final token that
+    belongs to each sequence."""
+    wl = W.random_workload(seed, max_new=30)
+    m = O.batch_metadata(wl.n_new, wl.seen, wl.block_lists, wl.block_size)
+    rows = np.arange(wl.T * 3, dtype=np.float32).reshape(wl.T, 3)
+    got = O.logits_gather(rows, m["cu_seqlens"])
+    last = {}
+    for t, i in enumerate(m["token_to_seq"]):
+        last[int(i)] = t
+    assert np.array_equal(got, rows[[last[i] for i in range(wl.S)]])
+
+
+def test_embedding_gather_bit_patterns_and_range():
+    """Rows move bit for bit (bf16 patterns, NaN payloads included) and only ids in
+    [0, vocab) read the table."""
+    table = np.array([[0x7FC1, 0x0001], [0x8000, 0xFFFF]], dtype=np.uint16)
+    got = O.embedding_gather(table, [1, 0, 2, -5, 1])
+    assert got.tolist() == [[0x8000, 0xFFFF], [0x7FC1, 0x0001], [0, 0], [0, 0],
+                            [0x8000, 0xFFFF]]
+    assert got.dtype == np.uint16
