@@ -82,6 +82,7 @@ KERNEL_GROUPS = {
     "meta_build.hip": ("meta_build.hip", ("meta_build_kernel",)),
     "gather.hip/embedding": ("gather.hip", ("embedding_gather_kernel",)),
     "gather.hip/logits": ("gather.hip", ("logits_gather_kernel",)),
+    "kv_offload.hip": ("kv_offload.hip", ("kv_block_copy_kernel",)),
 }
 
 
@@ -361,6 +362,66 @@ def gathers_leg(wl, eng, stream, reps=20, warm=3):
     return res
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16 per direction, the MI355X host link
+
+
+def kv_offload_leg(wl, eng, pool, stream, n=1024, reps=5, warm=2):
+    """KV block offload and restore of n scattered pool blocks (seeded choice) through a
+    page-locked host buffer, against plain contiguous copies of the same byte count
+    between device memory and page-locked host memory (the host link's copy rate).
+    Restore writes into other blocks than those offloaded; the pool's contents are not
+    needed afterwards."""
+    import torch
+
+    import ragged_blocked_kv_amd as R
+
+    dev = torch.device("cuda:0")
+    n = min(n, wl.num_blocks // 2)
+    perm = np.random.default_rng(17).permutation(wl.num_blocks).astype(np.int32)
+    src_ids, dst_ids = perm[:n], perm[n:2 * n]
+    st, nbytes = R.rbkv_kv_host_bytes(eng.shape, n)
+    R.check(st, "rbkv_kv_host_bytes")
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    payload = n * (wl.pool_bytes() // wl.num_blocks)
+    dev_buf = torch.empty(payload, dtype=torch.uint8, device=dev)
+    host_buf = torch.empty(payload, dtype=torch.uint8, pin_memory=True)
+
+    def timed(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def offload():
+        R.check(R.blocked_kv_offload(eng.shape, pool, src_ids, host, nbytes, stream),
+                "blocked_kv_offload")
+
+    def restore():
+        R.check(R.blocked_kv_restore(eng.shape, pool, dst_ids, host, nbytes, stream),
+                "blocked_kv_restore")
+
+    t_off, t_res = timed(offload), timed(restore)
+    t_d2h = timed(lambda: host_buf.copy_(dev_buf, non_blocking=True))
+    t_h2d = timed(lambda: dev_buf.copy_(host_buf, non_blocking=True))
+    gb = lambda us: payload / (us * 1e-6) / 1e9
+    return {
+        "blocks": n, "bytes": payload,
+        "offload": {"us": round(t_off, 1), "GBs": round(gb(t_off), 1),
+                    "frac_link_copy": round(t_d2h / t_off, 3),
+                    "frac_pcie_peak": round(gb(t_off) / PCIE_PEAK_GBS, 3)},
+        "restore": {"us": round(t_res, 1), "GBs": round(gb(t_res), 1),
+                    "frac_link_copy": round(t_h2d / t_res, 3),
+                    "frac_pcie_peak": round(gb(t_res) / PCIE_PEAK_GBS, 3)},
+        "link_copy_GBs": {"d2h": round(gb(t_d2h), 1), "h2d": round(gb(t_h2d), 1)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -374,6 +435,7 @@ def main():
     ap.add_argument("--no-ledger", action="store_true", help="skip the ledger host-cost leg")
     ap.add_argument("--no-serving", action="store_true", help="skip the SplitFuse serving leg")
     ap.add_argument("--no-gathers", action="store_true", help="skip the row-gather leg")
+    ap.add_argument("--no-offload", action="store_true", help="skip the KV offload leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=5, default=None,
@@ -466,6 +528,7 @@ def main():
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
     gathers = None if args.no_gathers else gathers_leg(wl, eng, stream)
+    offload = None if args.no_offload else kv_offload_leg(wl, eng, pool, stream)
     serving = None if args.no_serving else serving_leg(wl, eng, qkv, pool, out, stream)
 
     phase_ms = {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
@@ -530,6 +593,7 @@ def main():
         "ledger": ledger,
         "splitfuse_serving": serving,
         "gathers": gathers,
+        "kv_offload": offload,
     }
     print(json.dumps(rec), flush=True)
 

@@ -249,6 +249,37 @@ rbkv_status ragged_embedding_gather(const rbkv_batch* batch, const int32_t* toke
 rbkv_status ragged_logits_gather(const rbkv_batch* batch, const void* rows, int32_t width,
                                  int32_t dtype, void* out, void* stream);
 
+/* KV block offload and restore ("DeepSpeed Inference v2 source tour", section "The
+ * front desk: put, query, can_schedule", and its overview list: besides the allocator's
+ * bookkeeping, the blocked KV cache can copy chosen blocks out to host memory to make
+ * room on the device and copy them back when their sequence runs again).
+ *
+ * The host buffer is page-locked memory (hipHostMalloc; torch pin_memory) of at least
+ * rbkv_kv_host_bytes(shape, n) bytes laid out as
+ *   [n][2][Hkv][bs][d]  the n blocks in list order (each exactly as in the pool)
+ *   [n] int32           block ids
+ * Both calls first write `block_ids` (a host array) into the id region, then enqueue one
+ * kernel on `stream` that copies every listed block straight between the pool and the
+ * host buffer; the buffer must stay untouched until the stream has passed that kernel.
+ * offload: host slab k <- pool block block_ids[k] (the pool is not modified; the id
+ *          region keeps the source ids as a manifest).
+ * restore: pool block block_ids[k] <- host slab k (slabs written by an earlier offload of
+ *          the same shape; the id region is overwritten with the destination ids, which
+ *          must be distinct).  No other pool element is touched.
+ * Errors: INVALID_ARG (NULL, n < 0, host buffer smaller than required), BLOCKS (an id
+ * out of range, or repeated in a restore), UNSUPPORTED (n too large for one launch),
+ * DEVICE_PTR (pool not device memory of this device, host buffer not page-locked across
+ * its whole range), HIP.  n = 0 is OK and does nothing. */
+rbkv_status rbkv_kv_host_bytes(const rbkv_shape* shape, int32_t n, size_t* bytes);
+
+rbkv_status blocked_kv_offload(const rbkv_shape* shape, const void* kv_pool, int32_t n,
+                               const int32_t* block_ids, void* host, size_t host_bytes,
+                               void* stream);
+
+rbkv_status blocked_kv_restore(const rbkv_shape* shape, void* kv_pool, int32_t n,
+                               const int32_t* block_ids, void* host, size_t host_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

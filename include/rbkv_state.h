@@ -141,7 +141,7 @@ rbkv_status rbkv_state_block_ids(const rbkv_state* s, int64_t uid, int32_t* ids,
  *                               *blocks = max_new_blocks
  * so *tokens is how many of the tokens fit and *blocks how many blocks they need.  A
  * sequence in the open batch counts its in-flight tokens as cached.
- * Errors: INVALID_ARG (NULL, max_new_tokens < 0, max_new_blocks < 0). */
+ * Errors: INVALID_ARG (NULL, max_new_tokens < 0, max_new_blocks < 0, uid offloaded). */
 rbkv_status rbkv_state_query(const rbkv_state* s, int64_t uid, int32_t max_new_tokens,
                              int32_t max_new_blocks, int32_t* tokens, int32_t* blocks);
 
@@ -205,6 +205,29 @@ rbkv_status rbkv_state_post_forward(rbkv_state* s);
 /* Retire a sequence: its blocks go back to the allocator and its slot is freed.
  * Errors: INVALID_ARG (s NULL, uid not tracked, uid in the open batch). */
 rbkv_status rbkv_state_flush(rbkv_state* s, int64_t uid);
+
+/* Offload a sequence's blocks ("DeepSpeed Inference v2 source tour", section "The front
+ * desk": chosen blocks are copied to host memory to make room on the device, and copied
+ * back when their sequence is scheduled again).  rbkv_state_offload writes the ids the
+ * sequence holds, in key order, to ids[0 .. *n - 1] (cap >= that count) and gives them
+ * back to the allocator; the sequence keeps its slot and cached count but holds no
+ * blocks until rbkv_state_restore.  The caller copies the blocks out with
+ * blocked_kv_offload on the stream that later reuses them, before anything that could
+ * write them.  While offloaded a sequence may only be restored or flushed: naming it in
+ * query, can_schedule, put or compose is INVALID_ARG, and rbkv_state_sequence reports 0
+ * blocks.
+ * Errors: INVALID_ARG (NULL, uid not tracked, in the open batch or already offloaded,
+ * cap too small). */
+rbkv_status rbkv_state_offload(rbkv_state* s, int64_t uid, int32_t* ids, int32_t cap,
+                               int32_t* n);
+
+/* Give an offloaded sequence ceil(cached / block_size) blocks again and write their ids,
+ * in key order, to ids[0 .. *n - 1]; the caller copies the offloaded blocks back into
+ * them with blocked_kv_restore.  Errors: INVALID_ARG (NULL, uid not tracked or not
+ * offloaded, cap too small), BLOCKS (not enough free blocks; nothing changes),
+ * HOST_MEMORY. */
+rbkv_status rbkv_state_restore(rbkv_state* s, int64_t uid, int32_t* ids, int32_t cap,
+                               int32_t* n);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ Parity status per function (what pins each one, in ``tests/test_oracle_pins.py``
                                            reading (parity unpinned beyond Hq = Hkv)
 * ``embedding_gather`` / ``logits_gather`` -- pinned: hand fixture, last token derived
                                            from token_to_seq
+* ``offload_blocks`` / ``restore_blocks``  -- pinned: hand example, round trip
 * ``state_manager`` (allocator, ledger,  -- pinned: hand-derived walk
   compose, kv_requirements, ServingLoop)   (``tests/golden/ledger_walk.txt``), token-by-token
                                            block-growth simulation, conservation invariants,
@@ -46,3 +47,4 @@ from .ragged_attention import (  # noqa: F401
     ragged_attention,
 )
 from .gather import embedding_gather, logits_gather  # noqa: F401
+from .kv_offload import offload_blocks, restore_blocks  # noqa: F401

@@ -151,6 +151,8 @@ class StateManager:
         return q["seen"] + q["in_flight"], len(q["blocks"])
 
     def query(self, uid, max_new_tokens, max_new_blocks):
+        if self.seqs.get(uid, {}).get("offloaded"):
+            raise ValueError("an offloaded sequence must be restored first")
         cached, held = self._cached_and_held(uid)
         return kv_requirements(cached, held, max_new_tokens, max_new_blocks, self.block_size)
 
@@ -160,6 +162,8 @@ class StateManager:
             raise ValueError("bad token counts")
         if len(set(uids)) != len(uids):
             raise ValueError("uid listed twice")
+        if any(self.seqs.get(u, {}).get("offloaded") for u in uids):
+            raise ValueError("an offloaded sequence must be restored first")
         if len(uids) > self.max_seqs:
             return "batch_seq_limit"
         if sum(n_new) > self.max_tokens:
@@ -200,6 +204,8 @@ class StateManager:
             raise ValueError("bad budget or pending count")
         if len(set(uids)) != len(uids):
             raise ValueError("uid listed twice")
+        if any(self.seqs.get(u, {}).get("offloaded") for u in uids):
+            raise ValueError("an offloaded sequence must be restored first")
         left = min(int(token_budget), self.max_tokens)
         free_left = self.free_blocks
         tracked = self.n_tracked
@@ -270,6 +276,30 @@ class StateManager:
             raise ValueError(f"uid {uid} is in the open batch")
         self.alloc.release(q["blocks"])
         del self.seqs[uid]
+
+    def offload(self, uid):
+        """Give up the blocks of a sequence (returned in key order) and keep its place and
+        cached count; it must be restored before it runs again."""
+        uid = int(uid)
+        q = self.seqs.get(uid)
+        if q is None or q.get("offloaded") or (self.open is not None and uid in self.open):
+            raise ValueError(f"uid {uid} cannot be offloaded")
+        ids = list(q["blocks"])
+        self.alloc.release(ids)
+        q["blocks"] = []
+        q["offloaded"] = True
+        return ids
+
+    def restore(self, uid):
+        """New blocks, ceil(cached / bs) of them, for an offloaded sequence (key order)."""
+        uid = int(uid)
+        q = self.seqs.get(uid)
+        if q is None or not q.get("offloaded"):
+            raise ValueError(f"uid {uid} is not offloaded")
+        ids = self.alloc.allocate(ceil_div(q["seen"], self.block_size))
+        q["blocks"] = list(ids)
+        q["offloaded"] = False
+        return ids
 
 
 class ServingLoop:

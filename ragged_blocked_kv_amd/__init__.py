@@ -20,7 +20,7 @@ __all__ = [
     "rbkv_metadata_bytes", "rbkv_workspace_bytes", "ragged_batch_finalize",
     "blocked_kv_append_rotary", "ragged_blocked_attention", "ragged_batch_rebuild",
     "ragged_blocked_attention_phase", "ragged_embedding_gather", "ragged_logits_gather",
-    "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
+    "rbkv_kv_host_bytes", "blocked_kv_offload", "blocked_kv_restore", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
     "PHASE_DECODE", "PHASE_COMBINE",
     "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
     "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "ERR_HOST_MEMORY", "DTYPE_F32", "DTYPE_BF16",
@@ -44,6 +44,9 @@ EXPORTED_SYMBOLS = (
     "ragged_blocked_attention_phase",
     "ragged_embedding_gather",
     "ragged_logits_gather",
+    "rbkv_kv_host_bytes",
+    "blocked_kv_offload",
+    "blocked_kv_restore",
     # include/rbkv_state.h (bound in ragged_blocked_kv_amd.state)
     "rbkv_allocator_create",
     "rbkv_allocator_destroy",
@@ -63,6 +66,8 @@ EXPORTED_SYMBOLS = (
     "rbkv_state_finalize",
     "rbkv_state_post_forward",
     "rbkv_state_flush",
+    "rbkv_state_offload",
+    "rbkv_state_restore",
 )
 
 
@@ -140,6 +145,13 @@ def lib():
         L.ragged_logits_gather.argtypes = [
             ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_void_p]
+        L.rbkv_kv_host_bytes.restype = ctypes.c_int32
+        L.rbkv_kv_host_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+        for fn in (L.blocked_kv_offload, L.blocked_kv_restore):
+            fn.restype = ctypes.c_int32
+            fn.argtypes = [ctypes.POINTER(Shape), ctypes.c_void_p, ctypes.c_int32, _P,
+                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.ragged_blocked_attention.restype = ctypes.c_int32
         L.ragged_blocked_attention.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
@@ -254,3 +266,26 @@ def ragged_embedding_gather(batch: Batch, token_ids, table, vocab: int, width: i
 def ragged_logits_gather(batch: Batch, rows, width: int, dtype, out, stream=None) -> int:
     return lib().ragged_logits_gather(ctypes.byref(batch), _ptr(rows), int(width),
                                       int(_dtype_code(dtype)), _ptr(out), _stream(stream))
+
+
+def rbkv_kv_host_bytes(shape: Shape, n: int):
+    """(status, bytes) of the page-locked buffer that holds n offloaded blocks."""
+    b = ctypes.c_size_t(0)
+    st = lib().rbkv_kv_host_bytes(ctypes.byref(shape), int(n), ctypes.byref(b))
+    return st, b.value
+
+
+def _kv_transfer(fn, shape, kv_pool, block_ids, host, host_bytes, stream):
+    ids = np.ascontiguousarray(np.asarray(block_ids, dtype=np.int32))
+    return fn(ctypes.byref(shape), _ptr(kv_pool), int(ids.size), ids.ctypes.data_as(_P),
+              _ptr(host), int(host_bytes), _stream(stream))
+
+
+def blocked_kv_offload(shape: Shape, kv_pool, block_ids, host, host_bytes, stream=None) -> int:
+    return _kv_transfer(lib().blocked_kv_offload, shape, kv_pool, block_ids, host, host_bytes,
+                        stream)
+
+
+def blocked_kv_restore(shape: Shape, kv_pool, block_ids, host, host_bytes, stream=None) -> int:
+    return _kv_transfer(lib().blocked_kv_restore, shape, kv_pool, block_ids, host, host_bytes,
+                        stream)

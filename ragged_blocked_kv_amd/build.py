@@ -29,6 +29,7 @@ SOURCES = [
     "attn_prefill.hip",
     "attn_combine.hip",
     "gather.hip",
+    "kv_offload.hip",
 ]
 
 COMMON_FLAGS = [

@@ -430,6 +430,91 @@ rbkv_status ragged_logits_gather(const rbkv_batch* batch, const void* rows, int3
   return RBKV_OK;
 }
 
+namespace {
+
+size_t kv_block_bytes(const rbkv_shape& s) {
+  return (size_t)2 * s.n_kv_heads * s.block_size * s.head_dim * elem_bytes(s);
+}
+
+// Device view of a page-locked host range [p, p + bytes): both ends must be page-locked
+// host memory mapped at consecutive device addresses.
+rbkv_status pinned_range(void* p, size_t bytes, char** dev) {
+  hipPointerAttribute_t a, b;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess ||
+      hipPointerGetAttributes(&b, (char*)p + bytes - 1) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_DEVICE_PTR;
+  }
+  if (a.type != hipMemoryTypeHost || b.type != hipMemoryTypeHost || !a.devicePointer ||
+      (char*)b.devicePointer - (char*)a.devicePointer != (ptrdiff_t)(bytes - 1))
+    return RBKV_ERR_DEVICE_PTR;
+  *dev = (char*)a.devicePointer;
+  return RBKV_OK;
+}
+
+rbkv_status kv_transfer(int dir, const rbkv_shape* shape, void* pool, int32_t n,
+                        const int32_t* ids, void* host, size_t host_bytes, void* stream) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (n < 0 || !pool || !host || (n > 0 && !ids)) return RBKV_ERR_INVALID_ARG;
+  if (n == 0) return RBKV_OK;
+  const rbkv_shape& s = *shape;
+  size_t need = 0;
+  if ((st = rbkv_kv_host_bytes(shape, n, &need)) != RBKV_OK) return st;
+  if (host_bytes < need) return RBKV_ERR_INVALID_ARG;
+  const size_t bb = kv_block_bytes(s);
+  if ((uint64_t)n * ((bb + 16383) / 16384) * 256 >= (1ull << 32)) return RBKV_ERR_UNSUPPORTED;
+  for (int32_t k = 0; k < n; ++k)
+    if (ids[k] < 0 || ids[k] >= s.num_blocks) return RBKV_ERR_BLOCKS;
+  if (dir == 1) {  // destinations must be distinct
+    std::vector<uint8_t> used;
+    try {
+      used.assign((size_t)s.num_blocks, 0);
+    } catch (const std::bad_alloc&) {
+      return RBKV_ERR_HOST_MEMORY;
+    }
+    for (int32_t k = 0; k < n; ++k) {
+      if (used[(size_t)ids[k]]) return RBKV_ERR_BLOCKS;
+      used[(size_t)ids[k]] = 1;
+    }
+  }
+  if ((st = check_device(pool, (size_t)s.num_blocks * bb)) != RBKV_OK) return st;
+  char* hdev = nullptr;
+  if ((st = pinned_range(host, need, &hdev)) != RBKV_OK) return st;
+  // Stage the ids behind the slabs; the kernel reads them through the mapping.
+  const size_t ids_off = (size_t)n * bb;
+  memcpy((char*)host + ids_off, ids, (size_t)n * 4);
+  if (launch_kv_block_copy(dir, pool, hdev, (const int32_t*)(hdev + ids_off), n, bb,
+                           (hipStream_t)stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
+}  // namespace
+
+rbkv_status rbkv_kv_host_bytes(const rbkv_shape* shape, int32_t n, size_t* bytes) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (n < 0 || !bytes) return RBKV_ERR_INVALID_ARG;
+  *bytes = (size_t)n * kv_block_bytes(*shape) + (size_t)n * 4;
+  return RBKV_OK;
+}
+
+rbkv_status blocked_kv_offload(const rbkv_shape* shape, const void* kv_pool, int32_t n,
+                               const int32_t* block_ids, void* host, size_t host_bytes,
+                               void* stream) {
+  return kv_transfer(0, shape, const_cast<void*>(kv_pool), n, block_ids, host, host_bytes,
+                     stream);
+}
+
+rbkv_status blocked_kv_restore(const rbkv_shape* shape, void* kv_pool, int32_t n,
+                               const int32_t* block_ids, void* host, size_t host_bytes,
+                               void* stream) {
+  return kv_transfer(1, shape, kv_pool, n, block_ids, host, host_bytes, stream);
+}
+
 rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
                                      const void* qkv, const void* kv_pool, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream) {

@@ -145,4 +145,10 @@ hipError_t launch_gather_rows(int mode, const void* src, void* dst, const int32_
                               int32_t n_src, int32_t rows, size_t row_bytes,
                               hipStream_t stream);
 
+// Copies n pool blocks of block_bytes each between the pool and a host buffer mapped at
+// host_dev (dir 0: pool -> host, dir 1: host -> pool); ids_dev is the device view of the
+// staged block ids.  n * ceil(block_bytes / 16 KiB) * 256 < 2^32.
+hipError_t launch_kv_block_copy(int dir, void* pool, void* host_dev, const int32_t* ids_dev,
+                                int32_t n, size_t block_bytes, hipStream_t stream);
+
 }  // namespace rbkv

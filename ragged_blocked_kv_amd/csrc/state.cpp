@@ -142,6 +142,7 @@ struct Seq {
   int64_t uid = 0;
   int32_t seen = 0;       // tokens cached in the pool
   int32_t in_flight = 0;  // tokens of the open batch (0 when not in it)
+  bool offloaded = false;  // blocks given up; contents held by the caller on the host
   std::vector<int32_t> blocks;
 };
 
@@ -190,6 +191,7 @@ struct rbkv_state {
       const int32_t slot = index.find(uids[i]);
       looked_up[(size_t)i] = slot;
       if (slot >= 0) {
+        if (slots[(size_t)slot].offloaded) return false;  // must be restored first
         if (slot_stamp[(size_t)slot] == stamp) return false;  // listed twice
         slot_stamp[(size_t)slot] = stamp;
       } else {
@@ -374,12 +376,9 @@ rbkv_status rbkv_state_query(const rbkv_state* s, int64_t uid, int32_t max_new_t
   if (!s || !tokens || !blocks || max_new_tokens < 0 || max_new_blocks < 0)
     return RBKV_ERR_INVALID_ARG;
   const int32_t slot = s->index.find(uid);
-  int64_t cached = 0, held = 0;
-  if (slot >= 0) {
-    const Seq& q = s->slots[(size_t)slot];
-    cached = (int64_t)q.seen + q.in_flight;
-    held = (int64_t)q.blocks.size();
-  }
+  if (slot >= 0 && s->slots[(size_t)slot].offloaded) return RBKV_ERR_INVALID_ARG;
+  int64_t cached, held;
+  s->cached_held(slot, &cached, &held);
   const int64_t bs = s->cfg.block_size;
   const int64_t need = std::max<int64_t>(0, cdiv(cached + max_new_tokens, bs) - held);
   if (need <= max_new_blocks) {
@@ -479,6 +478,7 @@ rbkv_status rbkv_state_put(rbkv_state* s, int32_t n, const int64_t* uids, const 
       q.uid = uids[i];
       q.seen = 0;
       q.in_flight = 0;
+      q.offloaded = false;
       q.blocks.clear();
       s->index.insert(uids[i], slot);
     }
@@ -547,8 +547,49 @@ rbkv_status rbkv_state_flush(rbkv_state* s, int64_t uid) {
     q.blocks.clear();
   }
   q.seen = 0;
+  q.offloaded = false;
   s->index.erase(uid);
   s->free_slots.push_back(slot);  // capacity max_tracked_seqs: never allocates
+  return RBKV_OK;
+}
+
+rbkv_status rbkv_state_offload(rbkv_state* s, int64_t uid, int32_t* ids, int32_t cap,
+                               int32_t* n) {
+  if (!s || !n || cap < 0 || (cap > 0 && !ids)) return RBKV_ERR_INVALID_ARG;
+  const int32_t slot = s->index.find(uid);
+  if (slot < 0) return RBKV_ERR_INVALID_ARG;
+  Seq& q = s->slots[(size_t)slot];
+  if (q.offloaded || (s->open && q.in_flight > 0)) return RBKV_ERR_INVALID_ARG;
+  const int32_t held = (int32_t)q.blocks.size();
+  if (cap < held) return RBKV_ERR_INVALID_ARG;
+  std::copy(q.blocks.begin(), q.blocks.end(), ids);
+  s->alloc.give(held, q.blocks.data());
+  q.blocks.clear();
+  q.offloaded = true;
+  *n = held;
+  return RBKV_OK;
+}
+
+rbkv_status rbkv_state_restore(rbkv_state* s, int64_t uid, int32_t* ids, int32_t cap,
+                               int32_t* n) {
+  if (!s || !n || cap < 0 || (cap > 0 && !ids)) return RBKV_ERR_INVALID_ARG;
+  const int32_t slot = s->index.find(uid);
+  if (slot < 0) return RBKV_ERR_INVALID_ARG;
+  Seq& q = s->slots[(size_t)slot];
+  if (!q.offloaded) return RBKV_ERR_INVALID_ARG;
+  const int32_t need = (int32_t)cdiv(q.seen, s->cfg.block_size);
+  if (cap < need) return RBKV_ERR_INVALID_ARG;
+  if (need > s->alloc.n_free()) return RBKV_ERR_BLOCKS;
+  try {
+    q.blocks.reserve((size_t)need);
+  } catch (const std::bad_alloc&) {
+    return RBKV_ERR_HOST_MEMORY;
+  }
+  q.blocks.resize((size_t)need);
+  s->alloc.take(need, q.blocks.data());
+  std::copy(q.blocks.begin(), q.blocks.end(), ids);
+  q.offloaded = false;
+  *n = need;
   return RBKV_OK;
 }
 

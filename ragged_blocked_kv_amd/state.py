@@ -70,6 +70,8 @@ def _lib():
                                     ctypes.c_size_t, vp, ctypes.POINTER(Batch)],
             "rbkv_state_post_forward": [vp],
             "rbkv_state_flush": [vp, ctypes.c_int64],
+            "rbkv_state_offload": [vp, ctypes.c_int64, _PI32, _I32, _PI32],
+            "rbkv_state_restore": [vp, ctypes.c_int64, _PI32, _I32, _PI32],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -183,13 +185,18 @@ class StateManager:
               "rbkv_state_block_ids")
         return out[:n.value].copy()
 
-    def query(self, uid: int, max_new_tokens: int, max_new_blocks: int):
-        """(tokens, blocks) -- the KV requirements of ``max_new_tokens`` more tokens."""
+    def query_status(self, uid: int, max_new_tokens: int, max_new_blocks: int):
+        """(status, tokens, blocks) -- the KV requirements of ``max_new_tokens`` more
+        tokens."""
         t, b = ctypes.c_int32(), ctypes.c_int32()
-        check(_lib().rbkv_state_query(self._h, int(uid), int(max_new_tokens),
-                                      int(max_new_blocks), ctypes.byref(t), ctypes.byref(b)),
-              "rbkv_state_query")
-        return t.value, b.value
+        st = _lib().rbkv_state_query(self._h, int(uid), int(max_new_tokens),
+                                     int(max_new_blocks), ctypes.byref(t), ctypes.byref(b))
+        return st, t.value, b.value
+
+    def query(self, uid: int, max_new_tokens: int, max_new_blocks: int):
+        st, t, b = self.query_status(uid, max_new_tokens, max_new_blocks)
+        check(st, "rbkv_state_query")
+        return t, b
 
     def can_schedule_status(self, uids: Sequence[int], n_new: Sequence[int]):
         """(status, verdict)."""
@@ -276,6 +283,35 @@ class StateManager:
 
     def flush(self, uid: int) -> None:
         check(self.flush_status(uid), "rbkv_state_flush")
+
+    def _ids_call(self, fn, uid: int, cap: int):
+        out = np.zeros(max(int(cap), 1), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        st = fn(self._h, int(uid), out.ctypes.data_as(_PI32), int(cap), ctypes.byref(n))
+        return st, out[:n.value].copy()
+
+    def offload_status(self, uid: int):
+        """(status, ids): give up the blocks of ``uid`` (returned in key order)."""
+        info = self.sequence(uid)
+        cap = info[2] if info is not None else 0
+        return self._ids_call(_lib().rbkv_state_offload, uid, cap)
+
+    def offload(self, uid: int) -> np.ndarray:
+        st, ids = self.offload_status(uid)
+        check(st, "rbkv_state_offload")
+        return ids
+
+    def restore_status(self, uid: int):
+        """(status, ids): new blocks for an offloaded ``uid`` (in key order)."""
+        info = self.sequence(uid)
+        bs = self.config.block_size
+        cap = -(-info[0] // bs) if info is not None else 0
+        return self._ids_call(_lib().rbkv_state_restore, uid, cap)
+
+    def restore(self, uid: int) -> np.ndarray:
+        st, ids = self.restore_status(uid)
+        check(st, "rbkv_state_restore")
+        return ids
 
     @property
     def handle(self) -> Optional[int]:

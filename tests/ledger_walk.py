@@ -35,7 +35,7 @@ class OracleSide:
 
     def query(self, L, uid, m, b):
         st, r = self._call(lambda: L.query(uid, m, b))
-        return r if st == "ok" else st
+        return list(r) if st == "ok" else st
 
     def can_schedule(self, L, uids, n):
         st, r = self._call(lambda: L.can_schedule(uids, n))
@@ -48,6 +48,14 @@ class OracleSide:
     def compose(self, L, budget, uids, pending):
         st, r = self._call(lambda: L.compose(uids, pending, budget))
         return [(int(u), int(n)) for u, n in r] if st == "ok" else st
+
+    def offload(self, L, uid):
+        st, r = self._call(lambda: L.offload(uid))
+        return len(r) if st == "ok" else st
+
+    def restore(self, L, uid):
+        st, r = self._call(lambda: L.restore(uid))
+        return len(r) if st == "ok" else st
 
     def batch(self, L):
         st, r = self._call(lambda: L.batch())
@@ -96,7 +104,8 @@ class NativeSide:
         return self.S.BlockAllocator(n)
 
     def query(self, L, uid, m, b):
-        return L.query(uid, m, b)
+        st, t, n = L.query_status(uid, m, b)
+        return [t, n] if st == self.R.OK else self._status(st)
 
     def can_schedule(self, L, uids, n):
         st, v = L.can_schedule_status(uids, n)
@@ -111,6 +120,14 @@ class NativeSide:
         if st != self.R.OK:
             return self._status(st)
         return [(int(a), int(b)) for a, b in zip(u, n)]
+
+    def offload(self, L, uid):
+        st, ids = L.offload_status(uid)
+        return len(ids) if st == self.R.OK else self._status(st)
+
+    def restore(self, L, uid):
+        st, ids = L.restore_status(uid)
+        return len(ids) if st == self.R.OK else self._status(st)
 
     def batch(self, L):
         try:
@@ -178,8 +195,9 @@ def run(side, path=GOLDEN):
             A, named, held = side.allocator(n_alloc), {}, set()
             continue
         if op == "query":
-            got = list(side.query(L, int(args[0]), int(args[1]), int(args[2])))
-            ok = got == [int(x) for x in expect]
+            got = side.query(L, int(args[0]), int(args[1]), int(args[2]))
+            ok = (expect == ["invalid"] and got == "invalid") or \
+                (got != "invalid" and got == [int(x) for x in expect])
         elif op in ("can_schedule", "put"):
             uids, n = _pairs(args)
             got = getattr(side, op)(L, uids, n)
@@ -196,6 +214,9 @@ def run(side, path=GOLDEN):
         elif op in ("post_forward",):
             got = side.post_forward(L)
             ok = [got] == expect
+        elif op in ("offload", "restore"):
+            got = getattr(side, op)(L, int(args[0]))
+            ok = [str(got)] == expect
         elif op == "flush":
             got = side.flush(L, int(args[0]))
             ok = [got] == expect

@@ -201,3 +201,20 @@ def test_gather_validation_errors():
     # empty batches launch nothing and touch no pointer
     assert emb(batch=_fake_batch(S=0, T=0)) == R.OK
     assert lg(batch=_fake_batch(S=0, T=0)) == R.OK
+
+
+def test_kv_offload_validation_errors():
+    s = shape()  # 32 blocks of [2][2][16][64] bf16 = 8 KiB
+    st, b = R.rbkv_kv_host_bytes(s, 3)
+    assert st == R.OK and b == 3 * 2 * 2 * 16 * 64 * 2 + 3 * 4
+    assert R.rbkv_kv_host_bytes(s, -1)[0] == R.ERR_INVALID_ARG
+    assert R.rbkv_kv_host_bytes(shape(head_dim=96), 1)[0] == R.ERR_UNSUPPORTED
+    for fn in (R.blocked_kv_offload, R.blocked_kv_restore):
+        assert fn(s, FAKE, [0, 1, 2], FAKE, b - 1) == R.ERR_INVALID_ARG  # buffer too small
+        assert fn(s, None, [0], FAKE, b) == R.ERR_INVALID_ARG
+        assert fn(s, FAKE, [0], None, b) == R.ERR_INVALID_ARG
+        assert fn(s, FAKE, [0, 32, 1], FAKE, b) == R.ERR_BLOCKS       # out of range
+        assert fn(s, FAKE, [-1], FAKE, b) == R.ERR_BLOCKS
+        assert fn(s, FAKE, [], FAKE, 0) == R.OK                       # nothing to move
+    # a restore may not write one block twice; an offload may read one twice
+    assert R.blocked_kv_restore(s, FAKE, [4, 5, 4], FAKE, b) == R.ERR_BLOCKS

@@ -64,12 +64,19 @@ def _storage_numpy(x: torch.Tensor, dtype: str):
     return x.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else x.numpy()
 
 
+@pytest.mark.parametrize("preempt", ["recompute", "offload"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
-def test_serving_loop_matches_oracle(case):
+def test_serving_loop_matches_oracle(case, preempt):
+    """``preempt``: a sequence pushed out of a full pool is either flushed and fed again
+    from scratch ("recompute"), or has its blocks copied to host memory and released
+    ("offload"), to be restored into whatever blocks are free when room returns; its
+    history on the oracle side is never touched, so restored blocks must hold exactly
+    what was offloaded."""
+    import ragged_blocked_kv_amd as R
     from ragged_blocked_kv_amd.runtime import Engine
     from ragged_blocked_kv_amd.state import StateManager
 
-    print(f"serving loop {case.name}", flush=True)
+    print(f"serving loop {case.name} preempt={preempt}", flush=True)
     dev = torch.device("cuda:0")
     c = case
     max_context = c.max_prompt + c.max_gen + 1
@@ -97,8 +104,9 @@ def test_serving_loop_matches_oracle(case):
     tokens_of = {}  # uid -> tokens seen so far (for re-queueing a flushed sequence)
     finished = []
     owners = {}  # block id -> set of uids that held it
-    stats = dict(kv_limit=0, preempted=0, passes=0, prefill_tokens=0, decodes=0,
+    stats = dict(kv_limit=0, preempted=0, restored=0, passes=0, prefill_tokens=0, decodes=0,
                  max_err=0.0)
+    swapped = []  # (uid, pinned host buffer, its size), oldest first
 
     def both(fn_nat, fn_ora, what):
         st, v = fn_nat()
@@ -108,7 +116,7 @@ def test_serving_loop_matches_oracle(case):
         return o
 
     step = 0
-    while waiting or running:
+    while waiting or running or swapped:
         assert step < 400, "loop did not drain"
         # 1. flush finished sequences
         for u in [u for u in running if left[u] == 0]:
@@ -117,6 +125,23 @@ def test_serving_loop_matches_oracle(case):
             loop.flush(u)
             running.remove(u)
             finished.append(u)
+        # 1b. bring offloaded sequences back, oldest first, while their blocks fit
+        while swapped:
+            u, host, nbytes = swapped[0]
+            st, ids = nat.restore_status(u)
+            try:
+                ora.restore(u)
+                o_ok = True
+            except M.OracleBlocksError:
+                o_ok = False
+            assert (st == R.OK) == o_ok, (st, o_ok)
+            if st != R.OK:
+                assert st == R.ERR_BLOCKS
+                break
+            assert R.blocked_kv_restore(eng.shape, pool, ids, host, nbytes) == R.OK
+            swapped.pop(0)
+            running.append(u)
+            stats["restored"] += 1
         # 2. decodes of running sequences; preempt the youngest while they do not fit
         while True:
             decoding = set(running)
@@ -129,11 +154,19 @@ def test_serving_loop_matches_oracle(case):
             assert v == "kv_limit", v
             stats["kv_limit"] += 1
             u = running.pop()
-            nat.flush(u)
-            ora.flush(u)
-            loop.flush(u)
             stats["preempted"] += 1
-            waiting.insert(0, W.Request(u, step, tokens_of[u], left[u]))
+            if preempt == "offload":
+                ids = nat.offload(u)
+                assert len(ora.offload(u)) == len(ids)
+                st, nbytes = R.rbkv_kv_host_bytes(eng.shape, len(ids))
+                host = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+                assert R.blocked_kv_offload(eng.shape, pool, ids, host, nbytes) == R.OK
+                swapped.append((u, host, nbytes))
+            else:
+                nat.flush(u)
+                ora.flush(u)
+                loop.flush(u)
+                waiting.insert(0, W.Request(u, step, tokens_of[u], left[u]))
         # 3. admit arrived requests whole, in order, while the ledger says yes
         while waiting and waiting[0].arrival <= step:
             r = waiting[0]
@@ -192,12 +225,14 @@ def test_serving_loop_matches_oracle(case):
         stats["passes"] += 1
         step += 1
 
-    print(f"  {case.name}: {stats}", flush=True)
+    print(f"  {case.name} {preempt}: {stats}", flush=True)
     assert sorted(finished) == sorted(r.uid for r in trace)
     assert nat.counts() == (c.num_blocks, 0) == (ora.free_blocks, ora.n_tracked)
     # the loop exercised what it is for
     assert stats["kv_limit"] > 0, "pool never ran short"
     assert any(len(s) > 1 for s in owners.values()), "no block was reused"
+    if preempt == "offload":
+        assert stats["restored"] == stats["preempted"] > 0
 
 
 SPLITFUSE_CASES = [

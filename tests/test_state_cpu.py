@@ -142,14 +142,37 @@ def test_random_operations_match_oracle(seed):
             assert names.get(st, st) == o_st, (step, op, us, ns)
             if st == R.OK:
                 assert VERDICT_NAMES[v] == o_v, (step, op, us, ns)
-        elif r < 0.85:
+        elif r < 0.8:
             u = int(rng.choice(uids))
             o = oracle_call(lambda: ora.flush(u))[0]
             assert names.get(nat.flush_status(u), "?") == o, step
+        elif r < 0.85:
+            u = int(rng.choice(uids))
+            o_st, o_ids = oracle_call(lambda: ora.offload(u))
+            st, ids = nat.offload_status(u)
+            assert names.get(st, st) == o_st, step
+            if st == R.OK:
+                assert len(ids) == len(o_ids)
+        elif r < 0.9:
+            u = int(rng.choice(uids))
+            try:
+                o_st, o_n = "ok", len(ora.restore(u))
+            except ValueError:
+                o_st, o_n = "invalid", None
+            except M.OracleBlocksError:
+                o_st, o_n = "blocks", None
+            st, ids = nat.restore_status(u)
+            assert {R.OK: "ok", R.ERR_INVALID_ARG: "invalid", R.ERR_BLOCKS: "blocks"}[st] == o_st
+            if st == R.OK:
+                assert len(ids) == o_n
         else:
             u = int(rng.choice(uids))
             m, b = int(rng.integers(0, 70)), int(rng.integers(0, 6))
-            assert nat.query(u, m, b) == tuple(ora.query(u, m, b)), step
+            st, t, n = nat.query_status(u, m, b)
+            o_st, o_r = oracle_call(lambda: ora.query(u, m, b))
+            assert names.get(st, st) == o_st, step
+            if st == R.OK:
+                assert (t, n) == tuple(o_r), step
         assert nat.counts() == (ora.free_blocks, ora.n_tracked), step
         for u in uids:
             assert nat.sequence(u) == ora.sequence(u), (step, u)

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle as O
 import oracle.state_manager as M
 import workloads as W
 from ledger_walk import OracleSide, run
@@ -88,17 +89,28 @@ def test_ledger_invariants_under_random_operations(seed):
             L.post_forward()
         elif r < 0.75 and L.open is None:
             k = int(rng.integers(0, 4))
-            us = [int(u) for u in rng.choice(uids, size=k, replace=False)]
+            live = [u for u in uids if not L.seqs.get(u, {}).get("offloaded")]
+            us = [int(u) for u in rng.choice(live, size=min(k, len(live)), replace=False)]
             ns = [int(rng.integers(1, 20)) for _ in us]
             before = (L.free_blocks, L.n_tracked, {u: L.sequence(u) for u in uids})
             v = L.put(us, ns)
             verdicts.add(v)
             if v != "ok":  # a refused batch changes nothing
                 assert before == (L.free_blocks, L.n_tracked, {u: L.sequence(u) for u in uids})
-        else:
+        elif r < 0.85:
             u = int(rng.choice(uids))
             if u in L.seqs and (L.open is None or u not in L.open):
                 L.flush(u)
+        elif r < 0.93:
+            u = int(rng.choice(uids))
+            if u in L.seqs and not L.seqs[u].get("offloaded") and \
+                    (L.open is None or u not in L.open):
+                L.offload(u)
+        else:
+            u = int(rng.choice(uids))
+            if u in L.seqs and L.seqs[u].get("offloaded") and \
+                    M.ceil_div(L.seqs[u]["seen"], bs) <= L.free_blocks:
+                L.restore(u)
         # conservation and shape of the ledger
         lists = [q["blocks"] for q in L.seqs.values()]
         flat = [b for l in lists for b in l]
@@ -107,7 +119,8 @@ def test_ledger_invariants_under_random_operations(seed):
         assert len(flat) + L.free_blocks == cfg["num_blocks"]
         assert L.n_tracked <= cfg["max_tracked_seqs"]
         for q in L.seqs.values():
-            assert len(q["blocks"]) == M.ceil_div(q["seen"] + q["in_flight"], bs)
+            held = 0 if q.get("offloaded") else M.ceil_div(q["seen"] + q["in_flight"], bs)
+            assert len(q["blocks"]) == held
             assert q["seen"] + q["in_flight"] <= cfg["max_context"]
     assert "ok" in verdicts
 
@@ -225,3 +238,22 @@ def test_compose_fills_the_budget_when_nothing_else_binds():
     assert sum(n for _, n in batch) == 512
     assert [n for _, n in batch[:20]] == [1] * 20
     assert batch[20:] == [(120, 300), (121, 7), (122, 185)]  # the third prompt is cut
+
+
+def test_offload_restore_blocks_by_hand():
+    """Three blocks of one element pair each: offload [2, 0], restore them into [1, 2]."""
+    pool = np.arange(12, dtype=np.uint16).reshape(3, 2, 1, 1, 2)
+    host = O.offload_blocks(pool, [2, 0])
+    assert host.reshape(2, 4).tolist() == [[8, 9, 10, 11], [0, 1, 2, 3]]
+    back = O.restore_blocks(np.zeros_like(pool), [1, 2], host)
+    assert back.reshape(3, 4).tolist() == [[0, 0, 0, 0], [8, 9, 10, 11], [0, 1, 2, 3]]
+
+
+def test_offload_restore_round_trip():
+    rng = np.random.default_rng(3)
+    pool = rng.integers(0, 1 << 16, size=(9, 2, 2, 4, 8)).astype(np.uint16)
+    ids = [7, 1, 4, 0]
+    host = O.offload_blocks(pool, ids)
+    wiped = pool.copy()
+    wiped[ids] = 0
+    assert np.array_equal(O.restore_blocks(wiped, ids, host), pool)
