@@ -91,9 +91,10 @@ bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
   return memcmp(&a, &b, sizeof(rbkv_shape)) == 0;
 }
 
-// Split size for single-token decodes: about DECODE_TARGET_ITEMS items overall.
-int32_t choose_split_tiles(int64_t decode_tiles_total) {
-  int64_t st = cdiv64(decode_tiles_total, DECODE_TARGET_ITEMS);
+// Split size for single-token decodes: about the kernel's target number of items overall.
+int32_t choose_split_tiles(const rbkv_shape& s, int64_t decode_tiles_total) {
+  const int64_t target = decode_grouped(s) ? DECODE_TARGET_ITEMS_GROUPED : DECODE_TARGET_ITEMS;
+  int64_t st = cdiv64(decode_tiles_total, target);
   if (st < MIN_SPLIT_TILES) st = MIN_SPLIT_TILES;
   if (st > MAX_SPLIT_TILES) st = MAX_SPLIT_TILES;
   return (int32_t)st;
@@ -193,7 +194,7 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
     }
   }
 
-  const int32_t split = choose_split_tiles(dec_tiles);
+  const int32_t split = choose_split_tiles(s, dec_tiles);
   int64_t ndec = 0, npre = 0, npart = 0, ncomb = 0;
   int32_t npseq = 0, nqt_max = 0;
   for (int32_t i = 0; i < S; ++i) {

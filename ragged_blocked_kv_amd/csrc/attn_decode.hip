@@ -559,8 +559,9 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
   const int G = s.n_q_heads / s.n_kv_heads;
   if constexpr (sizeof(T) == 2) {
     // bf16 groups of 5 or more heads: one wave per head over shared LDS tiles.
-    if (G > 4 && G <= 8) return launch_group<D, 8>(s, b, qkv, pool, out, ws, stream);
-    if (G > 8) return launch_group<D, 16>(s, b, qkv, pool, out, ws, stream);
+    if (decode_grouped(s))
+      return G <= 8 ? launch_group<D, 8>(s, b, qkv, pool, out, ws, stream)
+                    : launch_group<D, 16>(s, b, qkv, pool, out, ws, stream);
   }
   if (G <= 1) return launch_t<T, D, 1>(s, b, qkv, pool, out, ws, stream);
   if (G <= 2) return launch_t<T, D, 2>(s, b, qkv, pool, out, ws, stream);

@@ -18,8 +18,11 @@ constexpr int MAX_GROUP = 16;
 constexpr int MAX_SEQS_LIMIT = 2048;
 constexpr int MAX_TOKENS_LIMIT = 1 << 20;
 constexpr int MAX_BLOCKS_LIMIT = 1 << 26;
-// Decode split-K sizing: aim for about this many decode work items per batch.
+// Decode split-K sizing: aim for about this many decode work items per batch (one
+// wavefront each), or DECODE_TARGET_ITEMS_GROUPED for the one-wave-per-head kernel
+// (a workgroup each, two resident per CU; finer items trim its tail).
 constexpr int64_t DECODE_TARGET_ITEMS = 6144;
+constexpr int64_t DECODE_TARGET_ITEMS_GROUPED = 12288;
 constexpr int MIN_SPLIT_TILES = 4;
 constexpr int MAX_SPLIT_TILES = 64;
 
@@ -30,6 +33,12 @@ enum HeaderWord {
 };
 
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Single-token decodes of bf16 groups of five or more query heads run on the
+// one-wave-per-head kernel (shared LDS tiles); everything else on one wave per item.
+inline bool decode_grouped(const rbkv_shape& s) {
+  return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads > 4;
+}
 
 // Tokens of one sequence per prefill workgroup: as many as fit PF_ROWS rows of G heads.
 __host__ __device__ inline int32_t q_tile_tokens(int32_t G) {
