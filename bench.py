@@ -534,6 +534,8 @@ def main():
     phase_ms = {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
                                   for k in range(args.steps)]))
                 for j, p in enumerate(PHASES)}
+    step_ev = np.array([events[k][0].elapsed_time(events[k][5]) for k in range(args.steps)])
+    attn_ev = np.array([events[k][2].elapsed_time(events[k][5]) for k in range(args.steps)])
     ms_per_step = wall * 1e3 / args.steps
     work = algorithmic_work(wl)
     dec_gbs = work["decode_bytes"] / (phase_ms["decode"] * 1e-3) / 1e9 if phase_ms["decode"] else 0
@@ -588,7 +590,13 @@ def main():
             "hbm_frac_decode": dec_gbs / HBM_PEAK_GBS,
             "mfma_frac_prefill": pre_tfs / MFMA_BF16_PEAK_TFS,
             "attention_algorithmic_GBs": work["attention_bytes"] / (attn_ms * 1e-3) / 1e9,
+            # every K/V row and Q/output of the batch once, over the whole attention time
+            "hbm_frac_attention": work["attention_bytes"] / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "us_p10_p50_p90": [round(float(np.percentile(attn_ev, q)) * 1e3, 1)
+                               for q in (10, 50, 90)],
         },
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_ev, q)) * 1e3, 1)
+                                for q in (10, 50, 90)],
         "finalize_host_and_upload_us": round(finalize_us, 1),
         "ledger": ledger,
         "splitfuse_serving": serving,

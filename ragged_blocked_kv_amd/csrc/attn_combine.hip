@@ -11,6 +11,7 @@ namespace rbkv {
 namespace {
 
 constexpr int CB_THREADS = 256;
+constexpr int CB_UNROLL = 8;  // splits whose partials are in flight together per lane
 
 template <typename T, int D>
 __global__ __launch_bounds__(CB_THREADS) void combine_kernel(
@@ -22,14 +23,35 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(
   for (int u = threadIdx.x; u < G * D; u += CB_THREADS) {
     const int h = u / D, dim = u % D;
     const float* p0 = ws + (size_t)slot0 * stride;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p0[s * stride + h]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float* p = p0 + s * stride;
-      const float c = exp2f(p[h] - M);
-      den = fmaf(c, p[G + h], den);
-      num = fmaf(c, p[2 * G + h * D + dim], num);
+    // One pass with a running maximum, CB_UNROLL splits at a time so that their loads
+    // overlap: rescaling by 2^(M_old - M_new) keeps num and den relative to the current
+    // maximum, which gives the same quotient as scaling everything by 2^(m_s - max m).
+    // The last batch re-reads the last split in its spare slots and gives them weight 0
+    // (m = -inf), so every batch issues all its loads at once.
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s = 0; s < ns; s += CB_UNROLL) {
+      float mv[CB_UNROLL], lv[CB_UNROLL], av[CB_UNROLL];
+#pragma unroll
+      for (int j = 0; j < CB_UNROLL; ++j) {
+        const float* p = p0 + (size_t)min(s + j, ns - 1) * stride;
+        mv[j] = s + j < ns ? p[h] : -INFINITY;
+        lv[j] = p[G + h];
+        av[j] = p[2 * G + h * D + dim];
+      }
+      float mb = mv[0];
+#pragma unroll
+      for (int j = 1; j < CB_UNROLL; ++j) mb = fmaxf(mb, mv[j]);
+      const float Mn = fmaxf(M, mb);
+      const float sc = exp2f(M - Mn);  // 0 on the first batch (M = -inf)
+      num *= sc;
+      den *= sc;
+#pragma unroll
+      for (int j = 0; j < CB_UNROLL; ++j) {
+        const float c = exp2f(mv[j] - Mn);
+        den = fmaf(c, lv[j], den);
+        num = fmaf(c, av[j], num);
+      }
+      M = Mn;
     }
     const float r = num / den;
     T* dst = out + ((size_t)token * Hq + (size_t)kvh * G + h) * D + dim;
