@@ -422,6 +422,34 @@ def kv_offload_leg(wl, eng, pool, stream, n=1024, reps=5, warm=2):
     }
 
 
+def concurrent_leg(wl, eng, qkv, pool, out, stream, steps=20, warm=5):
+    """The same step with ragged_blocked_attention_concurrent: the single-token decodes
+    on a second stream beside the prefill chunks (matrix cores), joined before the
+    split-K combine.  The phases read the same inputs and write disjoint output rows, so
+    they may run at once; the hardware then fills the CUs one phase leaves idle (a single
+    prefill chunk occupies a handful of CUs) with the other's workgroups.  Reported
+    beside the serial step, whose per-kernel times the roofline uses; here the kernels
+    share the chip, so only whole-step times are meaningful."""
+    import torch
+
+    def step():
+        eng.rebuild(stream=stream)
+        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
+        eng.attention_concurrent(qkv, pool, out, stream=stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": wl.T / (ms * 1e-3), "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -436,6 +464,8 @@ def main():
     ap.add_argument("--no-serving", action="store_true", help="skip the SplitFuse serving leg")
     ap.add_argument("--no-gathers", action="store_true", help="skip the row-gather leg")
     ap.add_argument("--no-offload", action="store_true", help="skip the KV offload leg")
+    ap.add_argument("--no-concurrent", action="store_true",
+                    help="skip the two-stream (prefill beside decode) step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=5, default=None,
@@ -527,6 +557,7 @@ def main():
 
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
+    concurrent = None if args.no_concurrent else concurrent_leg(wl, eng, qkv, pool, out, stream)
     gathers = None if args.no_gathers else gathers_leg(wl, eng, stream)
     offload = None if args.no_offload else kv_offload_leg(wl, eng, pool, stream)
     serving = None if args.no_serving else serving_leg(wl, eng, qkv, pool, out, stream)
@@ -598,6 +629,7 @@ def main():
         "step_us_p10_p50_p90": [round(float(np.percentile(step_ev, q)) * 1e3, 1)
                                 for q in (10, 50, 90)],
         "finalize_host_and_upload_us": round(finalize_us, 1),
+        "concurrent_phases": concurrent,
         "ledger": ledger,
         "splitfuse_serving": serving,
         "gathers": gathers,

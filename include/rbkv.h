@@ -226,6 +226,26 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
                                            void* out, void* workspace, size_t workspace_bytes,
                                            void* stream);
 
+/* ragged_blocked_attention with its two independent phases running at once: the
+ * single-token decodes on `side_stream`, the matrix-core prefill chunks on `stream`,
+ * then the split-K combine on `stream` once both are done.  The phases read the same
+ * inputs and write disjoint output rows, so the result is identical (bit for bit) to
+ * ragged_blocked_attention; the gain is that each phase's idle CUs (a batch with one
+ * prefill chunk keeps only a few busy, for example) run the other's workgroups.  The
+ * fork and join use two caller-owned events (hipEvent_t as void*, created by the
+ * caller, e.g. with hipEventDisableTiming): fork_event is recorded on `stream` and
+ * waited on by `side_stream`; join_event is recorded on `side_stream` and waited on by
+ * `stream`.  Both streams must be of the current device and must differ.  With no
+ * prefill or no decode work the call runs like ragged_blocked_attention on `stream`
+ * alone and leaves the events unused.  Graph-capturable like the rest (the standard
+ * event fork/join).  Errors: as ragged_blocked_attention, plus INVALID_ARG (NULL
+ * side_stream or event, side_stream == stream). */
+rbkv_status ragged_blocked_attention_concurrent(const rbkv_shape* shape, const rbkv_batch* batch,
+                                                const void* qkv, const void* kv_pool, void* out,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream, void* side_stream,
+                                                void* fork_event, void* join_event);
+
 /* The two row gathers that frame the layer stack over the same ragged batch ("DeepSpeed
  * Inference v2 source tour", section "Ragged batches: packing a whole server into four
  * tensors": the ragged embedding kernel gathers embedding rows for the packed token

@@ -19,7 +19,8 @@ __all__ = [
     "RbkvError", "Shape", "Batch", "lib", "status_string", "check",
     "rbkv_metadata_bytes", "rbkv_workspace_bytes", "ragged_batch_finalize",
     "blocked_kv_append_rotary", "ragged_blocked_attention", "ragged_batch_rebuild",
-    "ragged_blocked_attention_phase", "ragged_embedding_gather", "ragged_logits_gather",
+    "ragged_blocked_attention_phase", "ragged_blocked_attention_concurrent",
+    "ragged_embedding_gather", "ragged_logits_gather",
     "rbkv_kv_host_bytes", "blocked_kv_offload", "blocked_kv_restore", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
     "PHASE_DECODE", "PHASE_COMBINE",
     "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "blocked_kv_append_rotary",
     "ragged_blocked_attention",
     "ragged_blocked_attention_phase",
+    "ragged_blocked_attention_concurrent",
     "ragged_embedding_gather",
     "ragged_logits_gather",
     "rbkv_kv_host_bytes",
@@ -144,6 +146,11 @@ def lib():
         L.ragged_logits_gather.restype = ctypes.c_int32
         L.ragged_logits_gather.argtypes = [
             ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p]
+        L.ragged_blocked_attention_concurrent.restype = ctypes.c_int32
+        L.ragged_blocked_attention_concurrent.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p]
         L.rbkv_kv_host_bytes.restype = ctypes.c_int32
         L.rbkv_kv_host_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.c_int32,
@@ -289,3 +296,22 @@ def blocked_kv_offload(shape: Shape, kv_pool, block_ids, host, host_bytes, strea
 def blocked_kv_restore(shape: Shape, kv_pool, block_ids, host, host_bytes, stream=None) -> int:
     return _kv_transfer(lib().blocked_kv_restore, shape, kv_pool, block_ids, host, host_bytes,
                         stream)
+
+
+def _event(ev) -> Optional[int]:
+    if ev is None:
+        return None
+    if hasattr(ev, "cuda_event"):
+        return int(ev.cuda_event)
+    return int(ev)
+
+
+def ragged_blocked_attention_concurrent(shape: Shape, batch: Batch, qkv, kv_pool, out, workspace,
+                                        workspace_bytes: int, stream, side_stream, fork_event,
+                                        join_event) -> int:
+    """Events may be torch.cuda.Event objects that have been recorded once (torch creates
+    the underlying event on its first record) or raw hipEvent_t addresses."""
+    return lib().ragged_blocked_attention_concurrent(
+        ctypes.byref(shape), ctypes.byref(batch), _ptr(qkv), _ptr(kv_pool), _ptr(out),
+        _ptr(workspace), int(workspace_bytes), _stream(stream), _stream(side_stream),
+        _event(fork_event), _event(join_event))

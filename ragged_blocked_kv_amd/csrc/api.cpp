@@ -323,28 +323,25 @@ rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* 
   return RBKV_OK;
 }
 
-rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_batch* batch,
-                                           int32_t phase, const void* qkv, const void* kv_pool,
-                                           void* out, void* workspace, size_t workspace_bytes,
-                                           void* stream) {
+namespace {
+
+// Argument checks of an attention call (phases pre / dec / comb requested and non-empty).
+// *launch is false when there is nothing to launch (then no buffer is inspected).
+rbkv_status check_attention(const rbkv_shape* shape, const rbkv_batch* batch, bool pre,
+                            bool dec, bool comb, const void* qkv, const void* kv_pool,
+                            const void* out, const void* workspace, size_t workspace_bytes,
+                            bool* launch) {
+  *launch = false;
   rbkv_status st = check_shape(shape);
   if (st != RBKV_OK) return st;
   if (!batch || !qkv || !kv_pool || !out) return RBKV_ERR_INVALID_ARG;
-  if (phase < RBKV_PHASE_ALL || phase > RBKV_PHASE_COMBINE) return RBKV_ERR_INVALID_ARG;
   const rbkv_shape& s = *shape;
   if (!same_shape(batch->shape, s)) return RBKV_ERR_INVALID_ARG;
   if (batch->T < 0 || batch->T > s.max_tokens) return RBKV_ERR_INVALID_ARG;
   size_t need = 0;
   if ((st = rbkv_workspace_bytes(shape, batch, &need)) != RBKV_OK) return st;
   if (workspace_bytes < need || (need > 0 && !workspace)) return RBKV_ERR_WORKSPACE;
-  if (batch->T == 0) return RBKV_OK;
-  const bool pre = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_PREFILL) &&
-                   batch->n_prefill_items > 0;
-  const bool dec = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_DECODE) &&
-                   batch->n_decode_items > 0;
-  const bool comb = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_COMBINE) &&
-                    batch->n_combine_items > 0;
-  if (!pre && !dec && !comb) return RBKV_OK;
+  if (batch->T == 0 || (!pre && !dec && !comb)) return RBKV_OK;
   const size_t e = elem_bytes(s);
   const size_t qkv_bytes = (size_t)batch->T * (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * e;
   const size_t pool_bytes = (size_t)s.num_blocks * 2 * s.n_kv_heads * s.block_size * s.head_dim * e;
@@ -353,6 +350,28 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
   if ((st = check_device(kv_pool, pool_bytes)) != RBKV_OK) return st;
   if ((st = check_device(out, out_bytes)) != RBKV_OK) return st;
   if (need > 0 && (st = check_device(workspace, need)) != RBKV_OK) return st;
+  *launch = true;
+  return RBKV_OK;
+}
+
+}  // namespace
+
+rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_batch* batch,
+                                           int32_t phase, const void* qkv, const void* kv_pool,
+                                           void* out, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (phase < RBKV_PHASE_ALL || phase > RBKV_PHASE_COMBINE) return RBKV_ERR_INVALID_ARG;
+  const bool pre = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_PREFILL) && batch &&
+                   batch->n_prefill_items > 0;
+  const bool dec = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_DECODE) && batch &&
+                   batch->n_decode_items > 0;
+  const bool comb = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_COMBINE) && batch &&
+                    batch->n_combine_items > 0;
+  bool launch = false;
+  rbkv_status st = check_attention(shape, batch, pre, dec, comb, qkv, kv_pool, out, workspace,
+                                   workspace_bytes, &launch);
+  if (st != RBKV_OK || !launch) return st;
+  const rbkv_shape& s = *shape;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t err = hipSuccess;
   if (pre) err = launch_prefill(s, *batch, qkv, kv_pool, out, hs);
@@ -520,6 +539,45 @@ rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* 
                                      const void* qkv, const void* kv_pool, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   return ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_ALL, qkv, kv_pool, out,
+                                        workspace, workspace_bytes, stream);
+}
+
+rbkv_status ragged_blocked_attention_concurrent(const rbkv_shape* shape, const rbkv_batch* batch,
+                                                const void* qkv, const void* kv_pool, void* out,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream, void* side_stream,
+                                                void* fork_event, void* join_event) {
+  if (!side_stream || !fork_event || !join_event || side_stream == stream)
+    return RBKV_ERR_INVALID_ARG;
+  const bool pre = batch && batch->n_prefill_items > 0;
+  const bool dec = batch && batch->n_decode_items > 0;
+  if (!pre || !dec)
+    return ragged_blocked_attention(shape, batch, qkv, kv_pool, out, workspace,
+                                    workspace_bytes, stream);
+  // Every check (buffers included) before the fork, so an error launches nothing.
+  bool launch = false;
+  rbkv_status st = check_attention(shape, batch, pre, dec, batch->n_combine_items > 0, qkv,
+                                   kv_pool, out, workspace, workspace_bytes, &launch);
+  if (st != RBKV_OK || !launch) return st;
+  hipStream_t hs = (hipStream_t)stream, hside = (hipStream_t)side_stream;
+  hipEvent_t fork = (hipEvent_t)fork_event, join = (hipEvent_t)join_event;
+  if (hipEventRecord(fork, hs) != hipSuccess || hipStreamWaitEvent(hside, fork, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  st = ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_DECODE, qkv, kv_pool, out,
+                                      workspace, workspace_bytes, side_stream);
+  rbkv_status st2 = ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_PREFILL, qkv,
+                                                   kv_pool, out, workspace, workspace_bytes,
+                                                   stream);
+  // Join whatever was launched, so the caller's stream never runs ahead of the side work.
+  if (hipEventRecord(join, hside) != hipSuccess || hipStreamWaitEvent(hs, join, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  if (st != RBKV_OK) return st;
+  if (st2 != RBKV_OK) return st2;
+  return ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_COMBINE, qkv, kv_pool, out,
                                         workspace, workspace_bytes, stream);
 }
 

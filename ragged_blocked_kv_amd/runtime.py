@@ -11,7 +11,8 @@ import torch
 
 from . import (DTYPE_BF16, DTYPE_F32, Batch, Shape, blocked_kv_append_rotary, check,
                ragged_batch_finalize, ragged_batch_rebuild, ragged_blocked_attention,
-               ragged_blocked_attention_phase, ragged_embedding_gather, ragged_logits_gather,
+               ragged_blocked_attention_concurrent, ragged_blocked_attention_phase,
+               ragged_embedding_gather, ragged_logits_gather,
                rbkv_metadata_bytes, rbkv_workspace_bytes)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -35,6 +36,7 @@ class Engine:
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
         self.batch: Batch | None = None
         self._staged = None  # event after the last upload from host_pinned
+        self._side = self._fork = self._join = None  # for attention_concurrent
 
     @classmethod
     def for_workload(cls, wl, device="cuda"):
@@ -117,6 +119,21 @@ class Engine:
         check(ragged_logits_gather(batch or self.batch, rows, rows.shape[1],
                                    _DTYPE_CODE[rows.dtype], out, self.stream(stream)),
               "ragged_logits_gather")
+
+    def attention_concurrent(self, qkv, kv_pool, out, stream=None, batch=None):
+        """ragged_blocked_attention_concurrent: decodes on a side stream of this engine,
+        prefill chunks on ``stream``, joined before the combine (same result)."""
+        stream = self.stream(stream)
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)  # default priority
+            self._fork, self._join = torch.cuda.Event(), torch.cuda.Event()
+            # torch creates an event's handle on its first record
+            self._fork.record(stream)
+            self._join.record(stream)
+        check(ragged_blocked_attention_concurrent(
+            self.shape, batch or self.batch, qkv, kv_pool, out, self.workspace,
+            self.workspace.numel(), stream, self._side, self._fork, self._join),
+            "ragged_blocked_attention_concurrent")
 
     def new_out(self, T=None):
         T = self.batch.T if T is None else T

@@ -218,3 +218,17 @@ def test_kv_offload_validation_errors():
         assert fn(s, FAKE, [], FAKE, 0) == R.OK                       # nothing to move
     # a restore may not write one block twice; an offload may read one twice
     assert R.blocked_kv_restore(s, FAKE, [4, 5, 4], FAKE, b) == R.ERR_BLOCKS
+
+
+def test_concurrent_attention_argument_errors():
+    s = shape()
+    b = _fake_batch(S=2, T=5)
+    b.n_prefill_items, b.n_decode_items = 1, 1
+    f = lambda **kw: R.ragged_blocked_attention_concurrent(
+        kw.get("shape", s), b, FAKE, FAKE, FAKE, None, 0, kw.get("stream", 0x10),
+        kw.get("side", 0x20), kw.get("fork", 0x30), kw.get("join", 0x40))
+    assert f(side=None) == R.ERR_INVALID_ARG
+    assert f(fork=None) == R.ERR_INVALID_ARG
+    assert f(join=None) == R.ERR_INVALID_ARG
+    assert f(side=0x10) == R.ERR_INVALID_ARG  # the same stream twice
+    assert f(shape=shape(head_dim=96)) == R.ERR_UNSUPPORTED  # checked before any fork
