@@ -125,6 +125,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
+// The same with the non-temporal cache policy, for data read once.
+__device__ __forceinline__ void load_lds16_nt(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
+}
 
 // Wait until at most n vector-memory operations of this wave are outstanding (the LDS
 // DMA loads of later tiles stay in flight); expcnt and lgkmcnt are left alone.
