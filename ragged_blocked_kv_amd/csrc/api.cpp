@@ -74,12 +74,12 @@ rbkv_status check_pinned(const void* p) {
   return a.type == hipMemoryTypeHost ? RBKV_OK : RBKV_ERR_DEVICE_PTR;
 }
 
-rbkv_status launch_build(const rbkv_shape& s, char* dm, hipStream_t stream) {
+rbkv_status launch_build(const rbkv_shape& s, char* dm, int32_t S, hipStream_t stream) {
   const MetaLayout L = meta_layout(s);
   if (launch_meta_build((const int32_t*)dm, (int32_t*)(dm + L.cu), (int32_t*)(dm + L.kv_len),
                         (int32_t*)(dm + L.block_off), (int32_t*)(dm + L.tok2seq),
                         (int32_t*)(dm + L.pos), (int32_t*)(dm + L.dec), (int32_t*)(dm + L.pre),
-                        (int32_t*)(dm + L.comb), s.block_size, s.max_seqs, stream) !=
+                        (int32_t*)(dm + L.comb), s.block_size, s.max_seqs, S, stream) !=
       hipSuccess) {
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
@@ -281,7 +281,7 @@ rbkv_status ragged_batch_finalize(const rbkv_shape* shape, int32_t S, const int3
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
   }
-  if ((st = launch_build(s, dm, hs_stream)) != RBKV_OK) return st;
+  if ((st = launch_build(s, dm, S, hs_stream)) != RBKV_OK) return st;
   *out = b;
   return RBKV_OK;
 }
@@ -297,7 +297,7 @@ rbkv_status ragged_batch_rebuild(const rbkv_shape* shape, const rbkv_batch* batc
   char* dm = (char*)batch->seen - L.seen;
   if ((const char*)batch->cu_seqlens != dm + L.cu) return RBKV_ERR_INVALID_ARG;
   if ((st = check_device(dm, L.total)) != RBKV_OK) return st;
-  return launch_build(*shape, dm, (hipStream_t)stream);
+  return launch_build(*shape, dm, batch->S, (hipStream_t)stream);
 }
 
 rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* batch,

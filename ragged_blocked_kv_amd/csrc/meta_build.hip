@@ -1,6 +1,8 @@
-// Device metadata of one ragged batch, built by a single 1024-thread workgroup from the
-// staged per-sequence counts: cu_seqlens, kv_len, block_offsets, per-token owner and
-// absolute position, and the three attention work lists.  ("DeepSpeed Inference v2
+// Device metadata of one ragged batch, built from the staged per-sequence counts:
+// cu_seqlens, kv_len, block_offsets, per-token owner and absolute position, and the three
+// attention work lists.  Every 1024-thread workgroup plans all sequences and scans the
+// counts itself (a few microseconds, cheaper than a second launch or a grid-wide wait),
+// then writes the records of its own share of the sequences.  ("DeepSpeed Inference v2
 // source tour", section "Ragged batches: packing a whole server into four tensors":
 // token start/stop offsets, a tokens-to-sequence map and per-sequence block tables.)
 #include "rbkv_internal.h"
@@ -34,16 +36,6 @@ __device__ void wave_exclusive_scan(const int32_t* vals, int32_t* out, int S, in
   if (lane == 63) out[S] = incl;
 }
 
-// Largest i in [0, S) with off[i] <= x (off ascending, off[0] = 0 <= x).
-__device__ int upper_index(const int32_t* off, int S, int32_t x) {
-  int lo = 0, hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= x) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
     const int32_t* __restrict__ staging, int32_t* __restrict__ cu, int32_t* __restrict__ kv_len,
     int32_t* __restrict__ block_off, int32_t* __restrict__ tok2seq, int32_t* __restrict__ pos,
@@ -57,13 +49,10 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
 
   const int tid = threadIdx.x;
   const int32_t S = staging[H_S];
-  const int32_t T = staging[H_T];
   const int32_t split = staging[H_SPLIT];
   const int32_t Hkv = staging[H_HKV];
   const bool mfma = staging[H_MFMA] != 0;
   const int32_t qtt = staging[H_QTT];
-  const int32_t n_dec = staging[H_NDEC];
-  const int32_t n_comb = staging[H_NCOMB];
   const int32_t* n_new = staging + HDR_INTS;
   const int32_t* seen = n_new + max_seqs;
 
@@ -88,66 +77,96 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
   const int32_t* s_cu = offs[0];
   const int32_t* s_bo = offs[1];
   const int32_t* s_dec = offs[2];
-  const int32_t* s_pre = offs[3];
   const int32_t* s_part = offs[4];
   const int32_t* s_comb = offs[5];
 
-  for (int i = tid; i <= S; i += MB_THREADS) {
+  for (int i = blockIdx.x * MB_THREADS + tid; i <= S; i += gridDim.x * MB_THREADS) {
     cu[i] = s_cu[i];
     block_off[i] = s_bo[i];
     if (i < S) kv_len[i] = s_seen[i] + vals[0][i];
   }
-  for (int t = tid; t < T; t += MB_THREADS) {
-    const int i = upper_index(s_cu, S, t);
-    tok2seq[t] = i;
-    pos[t] = s_seen[i] + (t - s_cu[i]);
-  }
-  for (int w = tid; w < n_dec; w += MB_THREADS) {
-    const int i = upper_index(s_dec, S, w);
-    const int32_t local = w - s_dec[i];
-    const int32_t n = vals[0][i];
-    int4 r;
-    if (n == 1) {
-      const int32_t ns = s_nsplit[i];
-      r.x = s_cu[i];
-      r.y = local / ns;
-      r.z = local % ns;
-      r.w = ns > 1 ? s_part[i] + local : -1;
-    } else {  // one vector-ALU item per token of a float32 chunk, never split
-      r.x = s_cu[i] + local % n;
-      r.y = local / n;
-      r.z = 0;
-      r.w = -1;
+  // Per-token and per-item records.  Global wavefront w (of GW) takes sequences w, w + GW,
+  // w + 2 GW, ...; lane k first reads everything about the wavefront's k-th sequence from
+  // LDS in one go, then the wavefront walks its sequences with those values broadcast from
+  // their lane and its lanes write each sequence's consecutive entries, so no entry has to
+  // search for its sequence.
+  constexpr int N_WAVES = MB_THREADS / 64;
+  const int GW = gridDim.x * N_WAVES;
+  for (int i0 = blockIdx.x * N_WAVES + wave; i0 < S; i0 += GW * 64) {
+    const int il = i0 + GW * lane;
+    const bool have = il < S;
+    const int32_t l_n = have ? vals[0][il] : 0, l_base = have ? s_cu[il] : 0;
+    const int32_t l_seen = have ? s_seen[il] : 0, l_nd = have ? vals[2][il] : 0;
+    const int32_t l_dbase = have ? s_dec[il] : 0, l_nc = have ? vals[5][il] : 0;
+    const int32_t l_cbase = have ? s_comb[il] : 0, l_ns = have ? s_nsplit[il] : 1;
+    const int32_t l_part = have ? s_part[il] : 0;
+    const long long l_work = have ? s_pwork[il] : -1;
+    const int count = min(64, (S - i0 + GW - 1) / GW);
+    for (int k = 0; k < count; ++k) {
+      const int i = i0 + GW * k;
+      const int32_t n = __builtin_amdgcn_readlane(l_n, k);
+      const int32_t base = __builtin_amdgcn_readlane(l_base, k);
+      const int32_t sn = __builtin_amdgcn_readlane(l_seen, k);
+      for (int t = lane; t < n; t += 64) {
+        tok2seq[base + t] = i;
+        pos[base + t] = sn + t;
+      }
+      const int32_t nd = __builtin_amdgcn_readlane(l_nd, k);
+      const int32_t dbase = __builtin_amdgcn_readlane(l_dbase, k);
+      const int32_t ns = __builtin_amdgcn_readlane(l_ns, k);
+      const int32_t part = __builtin_amdgcn_readlane(l_part, k);
+      if (n == 1) {
+        for (int local = lane; local < nd; local += 64) {
+          int4 r;
+          r.x = base;
+          r.y = local / ns;
+          r.z = local % ns;
+          r.w = ns > 1 ? part + local : -1;
+          dec[dbase + local] = r;
+        }
+      } else {  // one vector-ALU item per token of a float32 chunk, never split
+        for (int local = lane; local < nd; local += 64) {
+          int4 r;
+          r.x = base + local % n;
+          r.y = local / n;
+          r.z = 0;
+          r.w = -1;
+          dec[dbase + local] = r;
+        }
+      }
+      const int32_t nc = __builtin_amdgcn_readlane(l_nc, k);
+      const int32_t cbase = __builtin_amdgcn_readlane(l_cbase, k);
+      for (int kvh = lane; kvh < nc; kvh += 64) {
+        int4 r;
+        r.x = base;
+        r.y = kvh;
+        r.z = part + kvh * ns;
+        r.w = ns;
+        comb[cbase + kvh] = r;
+      }
+      // Chunk sequences ranked by work, longest first (ties by batch order): the prefill
+      // kernel deals their (sequence, kv head) groups round-robin over the XCDs.  Each
+      // lane tests one sequence per step; a ballot counts those ranked ahead.
+      const long long wi = (long long)(
+          (unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(l_work >> 32), k) << 32 |
+          (uint32_t)__builtin_amdgcn_readlane((int)l_work, k));
+      if (wi >= 0) {
+        int32_t ahead = 0;
+        for (int j0 = 0; j0 < S; j0 += 64) {
+          const int j = j0 + lane;
+          const long long wj = j < S ? s_pwork[j] : -1;
+          ahead += __popcll(__ballot(wj > wi || (wj == wi && j < i)));
+        }
+        if (lane == 0) {
+          int4 r;
+          r.x = i;
+          r.y = (int32_t)cdiv64(n, qtt);
+          r.z = 0;
+          r.w = 0;
+          pre[ahead] = r;
+        }
+      }
     }
-    dec[w] = r;
-  }
-  // Chunk sequences ranked by work, longest first (ties by batch order): the prefill
-  // kernel deals their (sequence, kv head) groups round-robin over the XCDs.
-  for (int i = tid; i < S; i += MB_THREADS) {
-    const long long wi = s_pwork[i];
-    if (wi < 0) continue;
-    int32_t rank = 0;
-    for (int j = 0; j < S; ++j) {
-      const long long wj = s_pwork[j];
-      rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
-    }
-    int4 r;
-    r.x = i;
-    r.y = (int32_t)cdiv64(vals[0][i], qtt);
-    r.z = 0;
-    r.w = 0;
-    pre[rank] = r;
-  }
-  for (int w = tid; w < n_comb; w += MB_THREADS) {
-    const int i = upper_index(s_comb, S, w);
-    const int32_t kvh = w - s_comb[i];
-    const int32_t ns = s_nsplit[i];
-    int4 r;
-    r.x = s_cu[i];
-    r.y = kvh;
-    r.z = s_part[i] + kvh * ns;
-    r.w = ns;
-    comb[w] = r;
   }
 }
 
@@ -156,8 +175,10 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
 hipError_t launch_meta_build(const int32_t* staging, int32_t* cu, int32_t* kv_len,
                              int32_t* block_off, int32_t* tok2seq, int32_t* pos,
                              int32_t* dec, int32_t* pre, int32_t* comb, int32_t block_size,
-                             int32_t max_seqs, hipStream_t stream) {
-  hipLaunchKernelGGL(meta_build_kernel, dim3(1), dim3(MB_THREADS), 0, stream, staging, cu,
+                             int32_t max_seqs, int32_t S, hipStream_t stream) {
+  // About one sequence per wavefront: each wavefront's walk is then a short chain.
+  const int groups = (int)std::min<int64_t>(std::max<int64_t>(cdiv64(S, 16), 1), 128);
+  hipLaunchKernelGGL(meta_build_kernel, dim3(groups), dim3(MB_THREADS), 0, stream, staging, cu,
                      kv_len, block_off, tok2seq, pos, (int4*)dec, (int4*)pre, (int4*)comb,
                      block_size, max_seqs);
   return hipGetLastError();

@@ -134,7 +134,7 @@ inline size_t partial_floats(int32_t G, int32_t d) { return (size_t)G * (d + 2);
 hipError_t launch_meta_build(const int32_t* staging, int32_t* cu, int32_t* kv_len,
                              int32_t* block_off, int32_t* tok2seq, int32_t* pos,
                              int32_t* dec, int32_t* pre, int32_t* comb, int32_t block_size,
-                             int32_t max_seqs, hipStream_t stream);
+                             int32_t max_seqs, int32_t S, hipStream_t stream);
 
 hipError_t launch_append_rotary(const rbkv_shape& s, const rbkv_batch& b, void* qkv,
                                 void* pool, double rope_base, hipStream_t stream);
