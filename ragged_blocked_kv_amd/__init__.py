@@ -208,15 +208,27 @@ def rbkv_workspace_bytes(shape: Shape, batch: Batch):
 
 
 class _HostLists:
-    """Keeps the int32 host arrays alive for the duration of a finalize call."""
+    """Keeps the int32 host arrays alive for the duration of a finalize call.  The block
+    lists are packed into one flat array and the per-sequence pointers computed from its
+    offsets, so marshalling costs a few vector operations rather than one ctypes object
+    per sequence."""
 
     def __init__(self, n_new, seen, block_lists):
         self.n_new = np.ascontiguousarray(np.asarray(n_new, dtype=np.int32))
         self.seen = np.ascontiguousarray(np.asarray(seen, dtype=np.int32))
-        self.lists = [np.ascontiguousarray(np.asarray(b, dtype=np.int32)) for b in block_lists]
-        S = len(self.lists)
-        self.ptrs = (_P * max(S, 1))(*[l.ctypes.data_as(_P) for l in self.lists])
-        self.lens = np.ascontiguousarray(np.array([len(l) for l in self.lists], dtype=np.int32))
+        self.S = S = len(block_lists)
+        self.lens = np.fromiter(map(len, block_lists), dtype=np.int32, count=S)
+        flat = np.concatenate(block_lists, axis=None) if S else np.zeros(0, dtype=np.int32)
+        if flat.dtype != np.int32:
+            if flat.size and (flat.min() < -2**31 or flat.max() >= 2**31):
+                raise OverflowError("block id outside the int32 range")
+            flat = flat.astype(np.int32)
+        self.flat = np.ascontiguousarray(flat) if flat.size else np.zeros(1, dtype=np.int32)
+        offsets = np.zeros(max(S, 1), dtype=np.uintp)
+        if S > 1:
+            np.cumsum(self.lens[:-1], out=offsets[1:], dtype=np.uintp)
+        self.addrs = offsets * np.uintp(4) + np.uintp(self.flat.ctypes.data)
+        self.ptrs = self.addrs.ctypes.data_as(ctypes.POINTER(_P))
 
 
 def ragged_batch_finalize(shape: Shape, n_new: Sequence[int], seen: Sequence[int],
@@ -225,7 +237,7 @@ def ragged_batch_finalize(shape: Shape, n_new: Sequence[int], seen: Sequence[int
                           null_lists: bool = False):
     """(status, Batch).  ``host_pinned``/``dev_meta`` are tensors or raw addresses."""
     h = _HostLists(n_new, seen, block_lists)
-    S = len(h.lists) if S is None else S
+    S = h.S if S is None else S
     out = Batch()
     st = lib().ragged_batch_finalize(
         ctypes.byref(shape), int(S), h.n_new.ctypes.data_as(_P), h.seen.ctypes.data_as(_P),
