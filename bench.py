@@ -76,7 +76,8 @@ def measured_traffic(label, workload):
 # name fragments).  A label's record is valid while its source file hashes the same.
 KERNEL_GROUPS = {
     "attn_prefill.hip": ("attn_prefill.hip", ("prefill_attn_kernel",)),
-    "attn_decode.hip": ("attn_decode.hip", ("decode_attn_kernel", "decode_group_kernel")),
+    "attn_decode.hip": ("attn_decode.hip", ("decode_attn_kernel", "decode_group_kernel",
+                                            "decode_lean_kernel")),
     "append_rotary.hip": ("append_rotary.hip", ("append_rotary_kernel",)),
     "attn_combine.hip": ("attn_combine.hip", ("combine_kernel",)),
     "meta_build.hip": ("meta_build.hip", ("meta_build_kernel",)),
@@ -87,9 +88,15 @@ KERNEL_GROUPS = {
 
 
 def decode_kernel_name(wl):
-    """The decode kernel a workload runs: one wave per head for bf16 groups of 5+ heads."""
+    """The decode kernel a workload runs: bf16 runs one wave per head (a lean workgroup for
+    groups of up to 4 heads over 64-key blocks, the grouped one for 5+ heads); float32, and
+    bf16 over smaller blocks, one wave per item."""
     g = wl.n_q_heads // wl.n_kv_heads
-    return "decode_group_kernel" if wl.dtype == "bf16" and g > 4 else "decode_attn_kernel"
+    if wl.dtype == "bf16" and g > 4:
+        return "decode_group_kernel"
+    if wl.dtype == "bf16" and wl.block_size >= 64:
+        return "decode_lean_kernel"
+    return "decode_attn_kernel"
 
 
 def copy_calibration(nbytes, reps):

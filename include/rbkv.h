@@ -227,11 +227,13 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
                                            void* stream);
 
 /* ragged_blocked_attention with its two independent phases running at once: the
- * single-token decodes on `side_stream`, the matrix-core prefill chunks on `stream`,
- * then the split-K combine on `stream` once both are done.  The phases read the same
- * inputs and write disjoint output rows, so the result is identical (bit for bit) to
- * ragged_blocked_attention; the gain is that each phase's idle CUs (a batch with one
- * prefill chunk keeps only a few busy, for example) run the other's workgroups.  The
+ * matrix-core prefill chunks on `stream` (launched first), the single-token decodes on
+ * `side_stream`, then the split-K combine on `stream` once both are done.  The phases
+ * read the same inputs and write disjoint output rows, so the result is identical (bit
+ * for bit) to ragged_blocked_attention; the gain is that each phase's idle CUs (a batch
+ * with one prefill chunk keeps only a few busy, for example) run the other's workgroups,
+ * and that a bf16 decode workgroup of at most four heads over 64-key blocks fits on a CU
+ * beside a prefill workgroup.  The
  * fork and join use two caller-owned events (hipEvent_t as void*, created by the
  * caller, e.g. with hipEventDisableTiming): fork_event is recorded on `stream` and
  * waited on by `side_stream`; join_event is recorded on `side_stream` and waited on by

@@ -565,11 +565,11 @@ rbkv_status ragged_blocked_attention_concurrent(const rbkv_shape* shape, const r
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
   }
-  st = ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_DECODE, qkv, kv_pool, out,
-                                      workspace, workspace_bytes, side_stream);
   rbkv_status st2 = ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_PREFILL, qkv,
                                                    kv_pool, out, workspace, workspace_bytes,
                                                    stream);
+  st = ragged_blocked_attention_phase(shape, batch, RBKV_PHASE_DECODE, qkv, kv_pool, out,
+                                      workspace, workspace_bytes, side_stream);
   // Join whatever was launched, so the caller's stream never runs ahead of the side work.
   if (hipEventRecord(join, hside) != hipSuccess || hipStreamWaitEvent(hs, join, 0) != hipSuccess) {
     (void)hipGetLastError();
