@@ -2,9 +2,11 @@
 
 A step is one pass over one batch with every input already resident in HBM: the device
 metadata build (``ragged_batch_rebuild``), the rotary append
-(``blocked_kv_append_rotary``) and the attention (``ragged_blocked_attention``, issued as
-its prefill, decode and combine phases so that each kernel is timed with HIP events on
-the stream it runs on).  The batch is the full-budget mixed batch: 8192 new tokens over
+(``blocked_kv_append_rotary``) and the attention.  The timed steps run the attention as
+``ragged_blocked_attention_concurrent`` (prefill chunks and decodes sharing the chip on
+two streams, bit-identical output); a second, serial pass issues its prefill, decode and
+combine phases one after another so that each kernel is timed with HIP events on the
+stream it runs on (the roofline and the phase breakdown).  The batch is the full-budget mixed batch: 8192 new tokens over
 256 sequences (16 prefill chunks of 256..512 tokens and 240 decodes, seen ~ U[0, 8192]),
 GQA 32 query / 8 kv heads, head dim 128, 64-token blocks, bf16.  The host half of
 ``ragged_batch_finalize`` (validation, packing, the small host-to-device upload) runs once
@@ -429,34 +431,6 @@ def kv_offload_leg(wl, eng, pool, stream, n=1024, reps=5, warm=2):
     }
 
 
-def concurrent_leg(wl, eng, qkv, pool, out, stream, steps=20, warm=5):
-    """The same step with ragged_blocked_attention_concurrent: the single-token decodes
-    on a second stream beside the prefill chunks (matrix cores), joined before the
-    split-K combine.  The phases read the same inputs and write disjoint output rows, so
-    they may run at once; the hardware then fills the CUs one phase leaves idle (a single
-    prefill chunk occupies a handful of CUs) with the other's workgroups.  Reported
-    beside the serial step, whose per-kernel times the roofline uses; here the kernels
-    share the chip, so only whole-step times are meaningful."""
-    import torch
-
-    def step():
-        eng.rebuild(stream=stream)
-        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
-        eng.attention_concurrent(qkv, pool, out, stream=stream)
-
-    for _ in range(warm):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    return {"ms_per_step": round(ms, 4), "tokens_per_s": wl.T / (ms * 1e-3), "steps": steps}
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,8 +445,10 @@ def main():
     ap.add_argument("--no-serving", action="store_true", help="skip the SplitFuse serving leg")
     ap.add_argument("--no-gathers", action="store_true", help="skip the row-gather leg")
     ap.add_argument("--no-offload", action="store_true", help="skip the KV offload leg")
-    ap.add_argument("--no-concurrent", action="store_true",
-                    help="skip the two-stream (prefill beside decode) step")
+    ap.add_argument("--serial-only", action="store_true",
+                    help="time only the serial step (value from it): every library kernel then "
+                         "runs once per step with its whole work list, as the kernel-trace and "
+                         "counter profiles need")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a device copy of BYTES (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=5, default=None,
@@ -557,6 +533,8 @@ def main():
         eng.attention_phase(PHASE_COMBINE, qkv, pool, out, stream=stream)
         mark(5)
 
+    # Serial step with HIP events between the phases: the per-kernel times the roofline
+    # and the phase breakdown use.
     for _ in range(args.warmup):
         step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
@@ -565,11 +543,29 @@ def main():
     for k in range(args.steps):
         step(events[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_serial = time.perf_counter() - t0
+
+    # The timed step: the same work with the prefill and the decodes sharing the chip
+    # (ragged_blocked_attention_concurrent, bit-identical output), bracketed by
+    # synchronisations.
+    def step_concurrent():
+        eng.rebuild(stream=stream)
+        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
+        eng.attention_concurrent(qkv, pool, out, stream=stream)
+
+    wall = wall_serial
+    if not args.serial_only:
+        for _ in range(args.warmup):
+            step_concurrent()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            step_concurrent()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
-    concurrent = None if args.no_concurrent else concurrent_leg(wl, eng, qkv, pool, out, stream)
     gathers = None if args.no_gathers else gathers_leg(wl, eng, stream)
     offload = None if args.no_offload else kv_offload_leg(wl, eng, pool, stream)
     serving = None if args.no_serving else serving_leg(wl, eng, qkv, pool, out, stream)
@@ -623,7 +619,10 @@ def main():
             "head_dim": wl.head_dim,
             "block_size": wl.block_size,
             "kv_pool_blocks": wl.num_blocks,
-            "step": "metadata rebuild + rotary append + attention (prefill, decode, combine)",
+            "step": "metadata rebuild + rotary append + attention (prefill, decode, combine "
+                    "one after another)" if args.serial_only else
+                    "metadata rebuild + rotary append + attention (prefill chunks and decodes "
+                    "sharing the chip on two streams, then the split-K combine)",
         },
         "roofline": roof,
         "cpu_baseline": base,
@@ -641,7 +640,10 @@ def main():
         "step_us_p10_p50_p90": [round(float(np.percentile(step_ev, q)) * 1e3, 1)
                                 for q in (10, 50, 90)],
         "finalize_call_us": finalize_us,
-        "concurrent_phases": concurrent,
+        "serial_step": {"ms_per_step": wall_serial * 1e3 / args.steps,
+                        "tokens_per_s": wl.T * args.steps / wall_serial,
+                        "step": "the same phases one after another on one stream, with HIP "
+                                "events between them (the per-kernel times above)"},
         "ledger": ledger,
         "splitfuse_serving": serving,
         "gathers": gathers,

@@ -87,6 +87,18 @@ rbkv_status launch_build(const rbkv_shape& s, char* dm, int32_t S, hipStream_t s
   return RBKV_OK;
 }
 
+// Workspace: the split-K partials, then (when the two-stream call runs the decodes as
+// persistent workgroups) the 256-byte-aligned counter they claim items from.
+constexpr size_t CLAIM_BYTES = 256;
+bool uses_claim(const rbkv_shape& s, const rbkv_batch& b) {
+  return decode_lean_ok(s) && b.n_decode_items > 0 && b.n_prefill_items > 0;
+}
+size_t claim_offset(const rbkv_shape& s, const rbkv_batch& b) {
+  const int32_t G = s.n_q_heads / s.n_kv_heads;
+  const size_t partials = (size_t)b.n_partials * partial_floats(G, s.head_dim) * sizeof(float);
+  return uses_claim(s, b) ? (partials + CLAIM_BYTES - 1) / CLAIM_BYTES * CLAIM_BYTES : partials;
+}
+
 bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
   return memcmp(&a, &b, sizeof(rbkv_shape)) == 0;
 }
@@ -135,8 +147,7 @@ rbkv_status rbkv_workspace_bytes(const rbkv_shape* shape, const rbkv_batch* batc
   if (st != RBKV_OK) return st;
   if (!batch || !bytes) return RBKV_ERR_INVALID_ARG;
   if (!same_shape(batch->shape, *shape)) return RBKV_ERR_INVALID_ARG;
-  const int32_t G = shape->n_q_heads / shape->n_kv_heads;
-  *bytes = (size_t)batch->n_partials * partial_floats(G, shape->head_dim) * sizeof(float);
+  *bytes = claim_offset(*shape, *batch) + (uses_claim(*shape, *batch) ? CLAIM_BYTES : 0);
   return RBKV_OK;
 }
 
@@ -542,6 +553,50 @@ rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* 
                                         workspace, workspace_bytes, stream);
 }
 
+namespace {
+
+// The two-stream call for lean-decode shapes: persistent decode workgroups, two per CU,
+// start beside the prefill on the side stream and share the chip with it; once the
+// prefill is done a second launch of four per CU on the main stream joins them.  Both take
+// items from one counter, so they finish together whatever the split of the work.  (Sizes
+// measured on the full-budget and SplitFuse batches: one per CU beside the prefill, or
+// more than three, was slower; the second launch's size matters within 1-2%.)
+constexpr int OVERLAP_SIDE_WG_PER_CU = 2;
+constexpr int OVERLAP_MAIN_WG_PER_CU = 4;
+rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                                 const void* kv_pool, void* out, char* ws, hipStream_t hs,
+                                 hipStream_t hside, hipEvent_t fork, hipEvent_t join) {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu < 1) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  int32_t* claim = (int32_t*)(ws + claim_offset(s, b));
+  float* partials = (float*)ws;
+  bool ok = launch_decode_claim_reset(claim, hs) == hipSuccess &&
+            hipEventRecord(fork, hs) == hipSuccess &&
+            hipStreamWaitEvent(hside, fork, 0) == hipSuccess &&
+            launch_prefill(s, b, qkv, kv_pool, out, hs) == hipSuccess &&
+            launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
+                                     OVERLAP_SIDE_WG_PER_CU * n_cu, hside) == hipSuccess &&
+            launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
+                                     OVERLAP_MAIN_WG_PER_CU * n_cu, hs) == hipSuccess;
+  // Join whatever was launched, so the caller's stream never runs ahead of the side work.
+  const bool joined = hipEventRecord(join, hside) == hipSuccess &&
+                      hipStreamWaitEvent(hs, join, 0) == hipSuccess;
+  ok = ok && joined && (b.n_combine_items == 0 ||
+                        launch_combine(s, b, partials, out, hs) == hipSuccess);
+  if (!ok) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
+  return RBKV_OK;
+}
+
+}  // namespace
+
 rbkv_status ragged_blocked_attention_concurrent(const rbkv_shape* shape, const rbkv_batch* batch,
                                                 const void* qkv, const void* kv_pool, void* out,
                                                 void* workspace, size_t workspace_bytes,
@@ -561,6 +616,9 @@ rbkv_status ragged_blocked_attention_concurrent(const rbkv_shape* shape, const r
   if (st != RBKV_OK || !launch) return st;
   hipStream_t hs = (hipStream_t)stream, hside = (hipStream_t)side_stream;
   hipEvent_t fork = (hipEvent_t)fork_event, join = (hipEvent_t)join_event;
+  if (uses_claim(*shape, *batch))
+    return attention_overlapped(*shape, *batch, qkv, kv_pool, out, (char*)workspace, hs, hside,
+                                fork, join);
   if (hipEventRecord(fork, hs) != hipSuccess || hipStreamWaitEvent(hside, fork, 0) != hipSuccess) {
     (void)hipGetLastError();
     return RBKV_ERR_HIP;

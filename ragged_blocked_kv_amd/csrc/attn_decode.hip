@@ -14,6 +14,8 @@
 // "DeepSpeed Inference v2 source tour", section "Ragged batches: packing a whole server
 // into four tensors"; FlashAttention-2-style integration: "DeepSpeed-Inference and
 // DeepSpeed-MII", section 10.3.
+#include <algorithm>
+
 #include "rbkv_device.h"
 #include "rbkv_internal.h"
 
@@ -538,7 +540,8 @@ void decode_lean_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
     const int32_t* __restrict__ tok2seq, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
-    int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2) {
+    int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2,
+    int32_t* __restrict__ claim, int32_t n_items) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   constexpr int NT = 256;                    // threads
   constexpr int TILE_CHUNKS = 64 * CPR;      // chunks per K (or V) tile
@@ -550,7 +553,21 @@ void decode_lean_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Vt[64 * D];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int4 w = work[blockIdx.x];
+  // With a claim counter the workgroup is persistent: it takes item after item from the
+  // counter until the list is exhausted (the two-stream call runs the decodes as two such
+  // launches draining one list).  The claimed index is broadcast through the first word
+  // of the K tile, between barriers, before any tile load can overwrite it.
+  auto next_item = [&]() -> int32_t {
+    __syncthreads();  // every wave is done with the previous item's tile
+    if (tid == 0) *(volatile int32_t*)Kt = atomicAdd(claim, 1);
+    __syncthreads();
+    const int32_t it = __builtin_amdgcn_readfirstlane(*(volatile int32_t*)Kt);
+    __syncthreads();  // read by every wave before the next tile lands there
+    return it;
+  };
+  for (int32_t item = claim ? next_item() : (int32_t)blockIdx.x; item < n_items;
+       item = claim ? next_item() : n_items) {
+  const int4 w = work[item];
   const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
   const int32_t seq = tok2seq[token];
   const int32_t nkeys = pos[token] + 1;
@@ -677,7 +694,7 @@ void decode_lean_kernel(
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1) o[e] += __shfl_xor(o[e], off, 64);
   lsum = wave_sum_dpp(lsum);
-  if (wave >= G) return;  // padding head
+  if (wave >= G) continue;  // padding head
   if (slot < 0) {
     if (lane < CPR) {
       const float inv = 1.f / lsum;
@@ -698,19 +715,28 @@ void decode_lean_kernel(
       for (int e = 0; e < 8; ++e) dst[e] = o[e];
     }
   }
+  }  // items
 }
 
+// claim == nullptr: one workgroup per item.  Otherwise `workgroups` persistent
+// workgroups (at most one per item) drain the list through the counter.
 template <int D>
 hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
-                       const void* pool, void* out, float* ws, hipStream_t stream) {
+                       const void* pool, void* out, float* ws, hipStream_t stream,
+                       int32_t* claim = nullptr, int32_t workgroups = 0) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int G = s.n_q_heads / s.n_kv_heads;
-  hipLaunchKernelGGL((decode_lean_kernel<D>), dim3(b.n_decode_items), dim3(256), 0, stream,
+  const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
+  hipLaunchKernelGGL((decode_lean_kernel<D>), dim3(grid), dim3(256), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
                      (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
                      b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
-                     scale_log2);
+                     scale_log2, claim, b.n_decode_items);
   return hipGetLastError();
+}
+
+__global__ void lean_claim_reset_kernel(int32_t* claim) {
+  __hip_atomic_store(claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int NW>
@@ -773,6 +799,19 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
 }
 
 }  // namespace
+
+hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream) {
+  hipLaunchKernelGGL(lean_claim_reset_kernel, dim3(1), dim3(1), 0, stream, claim);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                                    const void* pool, void* out, float* ws, int32_t* claim,
+                                    int32_t workgroups, hipStream_t stream) {
+  return s.head_dim == 128
+             ? launch_lean<128>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+             : launch_lean<64>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+}
 
 hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                          const void* pool, void* out, float* ws, hipStream_t stream) {

@@ -149,6 +149,14 @@ hipError_t launch_append_rotary(const rbkv_shape& s, const rbkv_batch& b, void* 
 hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                          const void* pool, void* out, float* ws, hipStream_t stream);
 
+// The lean decode as persistent workgroups draining the decode list through a device
+// counter (decode_lean_ok shapes only); the counter must be zero when the first of the
+// launches sharing it starts (launch_decode_claim_reset).
+hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                                    const void* pool, void* out, float* ws, int32_t* claim,
+                                    int32_t workgroups, hipStream_t stream);
+hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream);
+
 hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                           const void* pool, void* out, hipStream_t stream);
 

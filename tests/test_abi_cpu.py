@@ -154,6 +154,30 @@ def test_append_and_attention_validation():
     assert R.blocked_kv_append_rotary(s, b, FAKE, FAKE, 1e4) == R.ERR_INVALID_ARG
 
 
+def test_workspace_holds_claim_counter_for_overlapped_decodes():
+    """bf16 batches with both phases, groups of <= 4 heads and 64-key blocks get a
+    256-byte-aligned item counter after the partials (the two-stream call's persistent
+    decodes claim items from it); other shapes and one-phase batches do not."""
+    def need(s, n_partials, n_dec, n_pre):
+        b = R.Batch()
+        b.shape = s
+        b.T = 3
+        b.n_partials, b.n_decode_items, b.n_prefill_items = n_partials, n_dec, n_pre
+        st, n = R.rbkv_workspace_bytes(s, b)
+        assert st == R.OK
+        return n
+    lean = shape(block_size=64)
+    part = 5 * 2 * (64 + 2) * 4                      # 2640 bytes of partials
+    assert need(lean, 5, 7, 2) == 2816 + 256         # partials rounded up to 256, + counter
+    assert need(lean, 0, 7, 2) == 256                # unsplit decodes: the counter alone
+    assert need(lean, 5, 7, 0) == part               # no prefill: no overlap, no counter
+    assert need(lean, 5, 0, 2) == part
+    assert need(shape(block_size=32), 5, 7, 2) == part          # blocks under 64 keys
+    assert need(shape(block_size=64, dtype="f32"), 5, 7, 2) == part
+    g8 = shape(block_size=64, n_q_heads=16, n_kv_heads=2)        # groups of 8 heads
+    assert need(g8, 5, 7, 2) == 5 * 8 * (64 + 2) * 4
+
+
 def test_valid_call_without_gpu_reports_pointer_kind():
     """With every argument valid the first HIP call is the pointer-kind check; on a
     machine without a GPU (or with fake addresses) it fails as DEVICE_PTR or HIP, never
