@@ -91,13 +91,14 @@ KERNEL_GROUPS = {
 
 def decode_kernel_name(wl):
     """The decode kernel a workload runs: bf16 runs one wave per head (a lean workgroup for
-    groups of up to 4 heads over 64-key blocks, the grouped one for 5+ heads); float32, and
-    bf16 over smaller blocks, one wave per item."""
+    groups of up to 8 heads over 64-key blocks, the two-stage grouped one for other groups
+    of 5+ heads); float32, and bf16 groups of up to 4 over smaller blocks, one wave per
+    item."""
     g = wl.n_q_heads // wl.n_kv_heads
+    if wl.dtype == "bf16" and g <= 8 and wl.block_size >= 64:
+        return "decode_lean_kernel"
     if wl.dtype == "bf16" and g > 4:
         return "decode_group_kernel"
-    if wl.dtype == "bf16" and wl.block_size >= 64:
-        return "decode_lean_kernel"
     return "decode_attn_kernel"
 
 

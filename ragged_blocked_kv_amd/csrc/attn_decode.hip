@@ -333,7 +333,8 @@ void decode_attn_kernel(
   }
 }
 
-// Grouped-query decode for bf16 caches: one wavefront per query head of the kv group
+// Grouped-query decode for bf16 caches (groups of 9-16 heads, and 5-8 heads over blocks of
+// fewer than 64 keys): one wavefront per query head of the kv group
 // (NW >= G waves; waves past G repeat the last head and write nothing).  Each 64-key K/V
 // tile is loaded once per workgroup, straight from HBM into LDS (global_load_lds), and
 // every wave streams its own head over it: Q in registers, one key per lane for Q.K (K
@@ -523,18 +524,21 @@ void decode_group_kernel(
   }
 }
 
-// Lean grouped decode: a workgroup that fits in what one prefill workgroup leaves free on
-// its CU (two waves of 208 registers on every SIMD and 128 KB of LDS), so the two-stream
-// attention call streams decode K/V through CUs whose matrix cores the prefill keeps busy.
-// Four wavefronts of at most 96 registers, one per query head (groups of up to four heads;
-// waves past G repeat the last head and write nothing), and one 64-key K/V tile in LDS
-// (32 KB at head dim 128) with nothing else there: the softmax weights reach the P.V lanes
-// through ds_bpermute, which needs no LDS allocation.  The tile is loaded straight from HBM
-// into LDS by all four waves; with one stage, a workgroup's loads wait while it computes,
-// and the latency is hidden by the other workgroups on the CU (five fit when no prefill is
-// there).  Work items, split-K partition and partial layout are those of the kernels above.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 5)))
+// Lean grouped decode for bf16 caches over blocks of at least 64 keys: NW (4 or 8)
+// wavefronts of at most 96 registers, one per query head of the kv group (waves past G
+// repeat the last head and write nothing), and one 64-key K/V tile in LDS (32 KB at head
+// dim 128) with nothing else there: the softmax weights reach the P.V lanes through
+// ds_bpermute, which needs no LDS allocation, and the query row sits in scalar registers.
+// The tile is loaded straight from HBM into LDS by all the waves from a uniform block base;
+// each lane copies its V chunks to registers before the barrier that frees the tile, so
+// the next tile's loads fly while P.V is summed, and the other workgroups on the CU (five
+// four-wave ones fit) hide the rest of the latency.  Arithmetic and order are those of the
+// kernels above (same results, bit for bit).  The four-wave workgroup also fits in what a
+// prefill workgroup leaves free on its CU (two waves of 208 registers per SIMD, 128 KB of
+// LDS).  Work items, split-K partition and partial layout are those of the kernels above;
+// with a claim counter the workgroups are persistent and take items from it.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5, 5)))
 void decode_lean_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
@@ -543,7 +547,7 @@ void decode_lean_kernel(
     int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2,
     int32_t* __restrict__ claim, int32_t n_items) {
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-  constexpr int NT = 256;                    // threads
+  constexpr int NT = NW * 64;                // threads
   constexpr int TILE_CHUNKS = 64 * CPR;      // chunks per K (or V) tile
   constexpr int NLD = TILE_CHUNKS / NT;      // direct loads per thread per K (or V) tile
   constexpr int KPI = 64 / CPR;              // P.V: keys per row group
@@ -720,14 +724,14 @@ void decode_lean_kernel(
 
 // claim == nullptr: one workgroup per item.  Otherwise `workgroups` persistent
 // workgroups (at most one per item) drain the list through the counter.
-template <int D>
+template <int D, int NW>
 hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                        const void* pool, void* out, float* ws, hipStream_t stream,
                        int32_t* claim = nullptr, int32_t workgroups = 0) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int G = s.n_q_heads / s.n_kv_heads;
   const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
-  hipLaunchKernelGGL((decode_lean_kernel<D>), dim3(grid), dim3(256), 0, stream,
+  hipLaunchKernelGGL((decode_lean_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
                      (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
                      b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
@@ -784,9 +788,11 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
                     void* out, float* ws, hipStream_t stream) {
   const int G = s.n_q_heads / s.n_kv_heads;
   if constexpr (sizeof(T) == 2) {
-    // bf16 groups of up to 4 heads over blocks of 64+ keys: one wave per head, one tile.
-    if (decode_lean_ok(s)) return launch_lean<D>(s, b, qkv, pool, out, ws, stream);
-    // bf16 groups of 5 or more heads: one wave per head over shared LDS tiles.
+    // bf16 groups of up to 8 heads over blocks of 64+ keys: one wave per head, one tile.
+    if (decode_lean_ok(s))
+      return G <= 4 ? launch_lean<D, 4>(s, b, qkv, pool, out, ws, stream)
+                    : launch_lean<D, 8>(s, b, qkv, pool, out, ws, stream);
+    // Other bf16 groups of 5 or more heads: one wave per head over two LDS tile stages.
     if (decode_grouped(s))
       return G <= 8 ? launch_group<D, 8>(s, b, qkv, pool, out, ws, stream)
                     : launch_group<D, 16>(s, b, qkv, pool, out, ws, stream);
@@ -808,9 +814,12 @@ hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream) {
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
                                     int32_t workgroups, hipStream_t stream) {
-  return s.head_dim == 128
-             ? launch_lean<128>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
-             : launch_lean<64>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+  const bool g4 = s.n_q_heads / s.n_kv_heads <= 4;
+  if (s.head_dim == 128)
+    return g4 ? launch_lean<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+              : launch_lean<128, 8>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+  return g4 ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+            : launch_lean<64, 8>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
 }
 
 hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,

@@ -40,11 +40,10 @@ inline bool decode_grouped(const rbkv_shape& s) {
   return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads > 4;
 }
 
-// Single-token decodes of bf16 groups of at most four query heads over blocks of 64 or
-// more keys run on the lean kernel (one wave per head, one K/V tile per workgroup), whose
-// footprint also fits beside a prefill workgroup on a CU.
+// Single-token decodes of bf16 groups of at most eight query heads over blocks of 64 or
+// more keys run on the lean kernel (one wave per head, one K/V tile per workgroup).
 inline bool decode_lean_ok(const rbkv_shape& s) {
-  return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads <= 4 && s.block_size >= 64;
+  return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads <= 8 && s.block_size >= 64;
 }
 
 // Tokens of one sequence per prefill workgroup: as many as fit PF_ROWS rows of G heads.

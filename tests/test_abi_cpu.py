@@ -155,7 +155,7 @@ def test_append_and_attention_validation():
 
 
 def test_workspace_holds_claim_counter_for_overlapped_decodes():
-    """bf16 batches with both phases, groups of <= 4 heads and 64-key blocks get a
+    """bf16 batches with both phases, groups of <= 8 heads and 64-key blocks get a
     256-byte-aligned item counter after the partials (the two-stream call's persistent
     decodes claim items from it); other shapes and one-phase batches do not."""
     def need(s, n_partials, n_dec, n_pre):
@@ -174,8 +174,10 @@ def test_workspace_holds_claim_counter_for_overlapped_decodes():
     assert need(lean, 5, 0, 2) == part
     assert need(shape(block_size=32), 5, 7, 2) == part          # blocks under 64 keys
     assert need(shape(block_size=64, dtype="f32"), 5, 7, 2) == part
-    g8 = shape(block_size=64, n_q_heads=16, n_kv_heads=2)        # groups of 8 heads
-    assert need(g8, 5, 7, 2) == 5 * 8 * (64 + 2) * 4
+    g8 = shape(block_size=64, n_q_heads=16, n_kv_heads=2)        # groups of 8 heads: counter
+    assert need(g8, 5, 7, 2) == 10752 + 256          # 10560 bytes of partials, rounded
+    g16 = shape(block_size=64, n_q_heads=32, n_kv_heads=2)       # groups of 16: none
+    assert need(g16, 5, 7, 2) == 5 * 16 * (64 + 2) * 4
 
 
 def test_valid_call_without_gpu_reports_pointer_kind():

@@ -33,9 +33,10 @@ def _run(wl, concurrent, reps=3):
 
 
 @pytest.mark.parametrize("name", ["random_bf16", "random_f32", "lean_g4_d128", "lean_g1_d64",
-                                  "lean_g2_unsplit", "splitfuse768_gqa4", "full8192_gqa4"])
+                                  "lean_g2_unsplit", "lean_g8_d128", "lean_g6_d64",
+                                  "splitfuse768_gqa4", "full8192_gqa4"])
 def test_concurrent_equals_serial(name):
-    """The lean-decode shapes (bf16, groups of up to 4 heads, 64-key blocks) take the
+    """The lean-decode shapes (bf16, groups of up to 8 heads, 64-key blocks) take the
     overlapped path: persistent decode workgroups on both streams drain one item counter;
     each item is still computed by one workgroup in the same order, so the bytes match."""
     print(f"concurrent {name}", flush=True)
@@ -48,6 +49,12 @@ def test_concurrent_equals_serial(name):
     elif name == "lean_g1_d64":
         wl = W.random_workload(34, dtype="bf16", n_q_heads=6, n_kv_heads=6, head_dim=64,
                                block_size=128, n_seqs=30, max_new=200, max_seen=2000)
+    elif name == "lean_g8_d128":
+        wl = W.random_workload(36, dtype="bf16", n_q_heads=32, n_kv_heads=4, head_dim=128,
+                               block_size=64, n_seqs=40, max_new=300, max_seen=3000)
+    elif name == "lean_g6_d64":
+        wl = W.random_workload(37, dtype="bf16", n_q_heads=12, n_kv_heads=2, head_dim=64,
+                               block_size=64, n_seqs=30, max_new=200, max_seen=2500)
     elif name == "lean_g2_unsplit":
         # short histories: every decode is one split, so the workspace holds the counter only
         wl = W.random_workload(35, dtype="bf16", n_q_heads=4, n_kv_heads=2, head_dim=128,
