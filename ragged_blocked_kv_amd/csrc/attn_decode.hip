@@ -563,9 +563,13 @@ void decode_lean_kernel(
   // of the K tile, between barriers, before any tile load can overwrite it.
   auto next_item = [&]() -> int32_t {
     __syncthreads();  // every wave is done with the previous item's tile
-    if (tid == 0) *(volatile int32_t*)Kt = atomicAdd(claim, 1);
+    if (tid == 0) {
+      const uint32_t c = (uint32_t)atomicAdd(claim, 1);
+      Kt[0] = (uint16_t)c;
+      Kt[1] = (uint16_t)(c >> 16);
+    }
     __syncthreads();
-    const int32_t it = __builtin_amdgcn_readfirstlane(*(volatile int32_t*)Kt);
+    const int32_t it = __builtin_amdgcn_readfirstlane((int32_t)(Kt[0] | ((uint32_t)Kt[1] << 16)));
     __syncthreads();  // read by every wave before the next tile lands there
     return it;
   };
