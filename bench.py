@@ -54,9 +54,19 @@ def algorithmic_work(wl):
     }
 
 
+def source_tokens_digest(text):
+    """Digest of C++/HIP source text with comments removed and whitespace collapsed, so
+    that edits to comments or layout alone keep a kernel's measured records valid."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def kernel_source_digest(name):
     p = os.path.join(ROOT, "ragged_blocked_kv_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    return source_tokens_digest(open(p).read())
 
 
 def measured_traffic(label, workload):

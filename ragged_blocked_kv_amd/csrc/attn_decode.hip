@@ -533,10 +533,12 @@ void decode_group_kernel(
 // each lane copies its V chunks to registers before the barrier that frees the tile, so
 // the next tile's loads fly while P.V is summed, and the other workgroups on the CU (five
 // four-wave ones fit) hide the rest of the latency.  Arithmetic and order are those of the
-// kernels above (same results, bit for bit).  The four-wave workgroup also fits in what a
-// prefill workgroup leaves free on its CU (two waves of 208 registers per SIMD, 128 KB of
-// LDS).  Work items, split-K partition and partial layout are those of the kernels above;
-// with a claim counter the workgroups are persistent and take items from it.
+// kernels above (same results, bit for bit).  Work items, split-K partition and partial
+// layout are those of the kernels above; with a claim counter the workgroups are
+// persistent and take items from it.  (A four-wave workgroup would also fit in what a
+// prefill workgroup leaves free on its CU, two waves of 208 registers per SIMD and 128 KB
+// of LDS; measured, sharing CUs that way was slower than letting the two kernels divide
+// the CUs between them.)
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5, 5)))
 void decode_lean_kernel(
@@ -575,154 +577,154 @@ void decode_lean_kernel(
   };
   for (int32_t item = claim ? next_item() : (int32_t)blockIdx.x; item < n_items;
        item = claim ? next_item() : n_items) {
-  const int4 w = work[item];
-  const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
-  const int32_t seq = tok2seq[token];
-  const int32_t nkeys = pos[token] + 1;
-  const int32_t tiles_total = (nkeys + 63) >> 6;
-  const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
-  const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
-  const int32_t key_end = min(nkeys, t_end * 64);
-  const int32_t* bids = block_ids + block_off[seq];
-  const int bsh = 31 - __builtin_clz(bs);  // block sizes are powers of two
-  const int32_t last_blk = (key_end - 1) >> bsh;
-  const size_t head_stride = (size_t)bs * D;
-  const size_t blk_stride = (size_t)2 * Hkv * head_stride;
-  const size_t v_off = (size_t)Hkv * head_stride;
-  const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
-  // This wave's head in the group, made provably uniform so that the query row is read
-  // into scalar registers (the vector registers cannot hold it beside the rest).
-  const int32_t hg = __builtin_amdgcn_readfirstlane(min(wave, G - 1));
+    const int4 w = work[item];
+    const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
+    const int32_t seq = tok2seq[token];
+    const int32_t nkeys = pos[token] + 1;
+    const int32_t tiles_total = (nkeys + 63) >> 6;
+    const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
+    const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
+    const int32_t key_end = min(nkeys, t_end * 64);
+    const int32_t* bids = block_ids + block_off[seq];
+    const int bsh = 31 - __builtin_clz(bs);  // block sizes are powers of two
+    const int32_t last_blk = (key_end - 1) >> bsh;
+    const size_t head_stride = (size_t)bs * D;
+    const size_t blk_stride = (size_t)2 * Hkv * head_stride;
+    const size_t v_off = (size_t)Hkv * head_stride;
+    const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
+    // This wave's head in the group, made provably uniform so that the query row is read
+    // into scalar registers (the vector registers cannot hold it beside the rest).
+    const int32_t hg = __builtin_amdgcn_readfirstlane(min(wave, G - 1));
 
-  // Direct load i of thread tid fills LDS chunk p = i*NT + tid of a tile (key row p / CPR);
-  // K chunks carry the XOR swizzle of the kernels above, V rows are stored as they are.
-  auto kswz = [](int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); };
-  auto fetch_ids = [&](int32_t t, int32_t* ids) { ids[0] = bids[min((t * 64) >> bsh, last_blk)]; };
-  const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[0]) + wave * 64 * 16);
-  const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vt[0]) + wave * 64 * 16);
-  // Loader lanes: row tid / CPR + i * (NT / CPR) of the tile, chunk tid % CPR; the K
-  // swizzle of a row depends on row % 16 only, which is the same for every i.
-  const int ld_r0 = tid / CPR, ld_c = tid % CPR;
-  const uint32_t ld_kc = (uint32_t)(ld_c ^ kswz(ld_r0)) * 16u, ld_vc = (uint32_t)ld_c * 16u;
-  // Blocks hold at least 64 keys, so a tile lies in one block: a uniform base and 32-bit
-  // lane offsets.  Rows past the end of the split load its last key (never read unmasked).
-  auto issue_tile = [&](int32_t t, const int32_t* ids) {
-    const int32_t key0 = t * 64;
-    const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
-    const int32_t rmax = key_end - 1 - key0;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const uint32_t roff = (uint32_t)min(ld_r0 + i * (NT / CPR), rmax) * (D * 2);
-      const uint32_t off = i * NT * 16;
-      load_lds16_nt_s(base, roff + ld_kc, k_dst0 + off);
-      load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + off);
+    // Direct load i of thread tid fills LDS chunk p = i*NT + tid of a tile (key row p / CPR);
+    // K chunks carry the XOR swizzle of the kernels above, V rows are stored as they are.
+    auto kswz = [](int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); };
+    auto fetch_ids = [&](int32_t t, int32_t* ids) { ids[0] = bids[min((t * 64) >> bsh, last_blk)]; };
+    const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[0]) + wave * 64 * 16);
+    const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vt[0]) + wave * 64 * 16);
+    // Loader lanes: row tid / CPR + i * (NT / CPR) of the tile, chunk tid % CPR; the K
+    // swizzle of a row depends on row % 16 only, which is the same for every i.
+    const int ld_r0 = tid / CPR, ld_c = tid % CPR;
+    const uint32_t ld_kc = (uint32_t)(ld_c ^ kswz(ld_r0)) * 16u, ld_vc = (uint32_t)ld_c * 16u;
+    // Blocks hold at least 64 keys, so a tile lies in one block: a uniform base and 32-bit
+    // lane offsets.  Rows past the end of the split load its last key (never read unmasked).
+    auto issue_tile = [&](int32_t t, const int32_t* ids) {
+      const int32_t key0 = t * 64;
+      const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
+      const int32_t rmax = key_end - 1 - key0;
+  #pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint32_t roff = (uint32_t)min(ld_r0 + i * (NT / CPR), rmax) * (D * 2);
+        const uint32_t off = i * NT * 16;
+        load_lds16_nt_s(base, roff + ld_kc, k_dst0 + off);
+        load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + off);
+      }
+    };
+
+    u32x4 q[CPR];
+    {
+      const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + hg) * D;
+  #pragma unroll
+      for (int c = 0; c < CPR; ++c) q[c] = ld16(qrow + c * 8);
     }
-  };
+    int32_t ids[1];
+    fetch_ids(t_begin, ids);
+    issue_tile(t_begin, ids);
+    fetch_ids(min(t_begin + 1, t_end - 1), ids);
 
-  u32x4 q[CPR];
-  {
-    const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + hg) * D;
-#pragma unroll
-    for (int c = 0; c < CPR; ++c) q[c] = ld16(qrow + c * 8);
-  }
-  int32_t ids[1];
-  fetch_ids(t_begin, ids);
-  issue_tile(t_begin, ids);
-  fetch_ids(min(t_begin + 1, t_end - 1), ids);
+    float m_run = -INFINITY, lsum = 0.f, o[8];
+  #pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    const int cl = lane % CPR, kg = lane / CPR;  // P.V: chunk column and key sub-row
+    // Q.K: byte offset of this lane's key row with its swizzle; chunk c of the row is at
+    // krow ^ 16c.  Re-declared opaque every tile so that the sixteen chunk addresses are
+    // recomputed (one XOR each) rather than held across the loop in registers.
+    uint32_t krow = (uint32_t)(lane * CPR + kswz(lane)) * 16u;
+    // P.V: byte offset of this lane's V chunk in row group 0 and the ds_bpermute address of
+    // the weight of its key in row group 0; row group i adds a constant (an instruction
+    // offset).  Opaque per tile for the same reason.
+    uint32_t vcol = (uint32_t)(kg * CPR + cl) * 16u;
+    uint32_t pidx = (uint32_t)kg * 4u;
 
-  float m_run = -INFINITY, lsum = 0.f, o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  const int cl = lane % CPR, kg = lane / CPR;  // P.V: chunk column and key sub-row
-  // Q.K: byte offset of this lane's key row with its swizzle; chunk c of the row is at
-  // krow ^ 16c.  Re-declared opaque every tile so that the sixteen chunk addresses are
-  // recomputed (one XOR each) rather than held across the loop in registers.
-  uint32_t krow = (uint32_t)(lane * CPR + kswz(lane)) * 16u;
-  // P.V: byte offset of this lane's V chunk in row group 0 and the ds_bpermute address of
-  // the weight of its key in row group 0; row group i adds a constant (an instruction
-  // offset).  Opaque per tile for the same reason.
-  uint32_t vcol = (uint32_t)(kg * CPR + cl) * 16u;
-  uint32_t pidx = (uint32_t)kg * 4u;
+    for (int32_t tt = t_begin; tt < t_end; ++tt) {
+      wait_vmcnt<0>();  // this wave's share of tile tt
+      __syncthreads();  // every wave's share
+      const int32_t key0 = tt * 64;
+      asm volatile("" : "+v"(krow), "+v"(vcol), "+v"(pidx));
 
-  for (int32_t tt = t_begin; tt < t_end; ++tt) {
-    wait_vmcnt<0>();  // this wave's share of tile tt
-    __syncthreads();  // every wave's share
-    const int32_t key0 = tt * 64;
-    asm volatile("" : "+v"(krow), "+v"(vcol), "+v"(pidx));
-
-    // Scores: lane = key.
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPR; ++c)
-      s = dot_chunk(q[c], *(const u32x4*)((const char*)Kt + (krow ^ (16u * c))), s, bf16_t{});
-    const float sc = key0 + lane < key_end ? s * scale_log2 : -INFINITY;
-    const float mn = fmaxf(m_run, wave_max_dpp(sc));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-    const float pe = __builtin_amdgcn_exp2f(sc - mn);
-    m_run = mn;
-    lsum = lsum * alpha + pe;
-    // P.V: lane accumulates the 8 columns of chunk cl over keys i*KPI + kg, two keys per
-    // v_dot2 (rows i and i+1 interleaved per column with v_perm_b32).  The lane's V
-    // chunks go into registers before the barrier, so the next tile's loads are issued
-    // first and fly while the products are summed; the weight of key r is then fetched
-    // from lane r (ds_bpermute reads no LDS memory).
-    u32x4 vr[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      vr[i] = *(const u32x4*)((const char*)Vt + vcol + i * (KPI * CPR * 16));
-    if (tt + 1 < t_end) {
-      __syncthreads();  // every wave is done with the tile before it is overwritten
-      issue_tile(tt + 1, ids);
-      fetch_ids(min(tt + 2, t_end - 1), ids);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= alpha;
-    const int pe_bits = __float_as_int(pe);
-#pragma unroll
-    for (int i = 0; i < NI; i += 2) {
-      const float pa = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(pidx + i * KPI * 4), pe_bits));
-      const float pb = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(pidx + (i + 1) * KPI * 4), pe_bits));
-      const bf16x2v pp = as_bf16x2(pack_bf16x2(pa, pb));
-      const uint32_t aw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-      const uint32_t bw[4] = {vr[i + 1].x, vr[i + 1].y, vr[i + 1].z, vr[i + 1].w};
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        o[2 * jj] = __builtin_amdgcn_fdot2_f32_bf16(
-            pp, as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x05040100u)), o[2 * jj], false);
-        o[2 * jj + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-            pp, as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x07060302u)), o[2 * jj + 1], false);
+      // Scores: lane = key.
+      float s = 0.f;
+  #pragma unroll
+      for (int c = 0; c < CPR; ++c)
+        s = dot_chunk(q[c], *(const u32x4*)((const char*)Kt + (krow ^ (16u * c))), s, bf16_t{});
+      const float sc = key0 + lane < key_end ? s * scale_log2 : -INFINITY;
+      const float mn = fmaxf(m_run, wave_max_dpp(sc));
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      const float pe = __builtin_amdgcn_exp2f(sc - mn);
+      m_run = mn;
+      lsum = lsum * alpha + pe;
+      // P.V: lane accumulates the 8 columns of chunk cl over keys i*KPI + kg, two keys per
+      // v_dot2 (rows i and i+1 interleaved per column with v_perm_b32).  The lane's V
+      // chunks go into registers before the barrier, so the next tile's loads are issued
+      // first and fly while the products are summed; the weight of key r is then fetched
+      // from lane r (ds_bpermute reads no LDS memory).
+      u32x4 vr[NI];
+  #pragma unroll
+      for (int i = 0; i < NI; ++i)
+        vr[i] = *(const u32x4*)((const char*)Vt + vcol + i * (KPI * CPR * 16));
+      if (tt + 1 < t_end) {
+        __syncthreads();  // every wave is done with the tile before it is overwritten
+        issue_tile(tt + 1, ids);
+        fetch_ids(min(tt + 2, t_end - 1), ids);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      const int pe_bits = __float_as_int(pe);
+  #pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        const float pa = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(pidx + i * KPI * 4), pe_bits));
+        const float pb = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(pidx + (i + 1) * KPI * 4), pe_bits));
+        const bf16x2v pp = as_bf16x2(pack_bf16x2(pa, pb));
+        const uint32_t aw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        const uint32_t bw[4] = {vr[i + 1].x, vr[i + 1].y, vr[i + 1].z, vr[i + 1].w};
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          o[2 * jj] = __builtin_amdgcn_fdot2_f32_bf16(
+              pp, as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x05040100u)), o[2 * jj], false);
+          o[2 * jj + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+              pp, as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x07060302u)), o[2 * jj + 1], false);
+        }
       }
     }
-  }
 
-  // Reduce over the lanes that share a chunk column, and the row sums over all lanes.
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1) o[e] += __shfl_xor(o[e], off, 64);
-  lsum = wave_sum_dpp(lsum);
-  if (wave >= G) continue;  // padding head
-  if (slot < 0) {
-    if (lane < CPR) {
-      const float inv = 1.f / lsum;
-      float r[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = o[e] * inv;
-      st16(out + ((size_t)token * Hq + (size_t)kvh * G + hg) * D + cl * 8, pack_chunk<bf16_t>(r));
+    // Reduce over the lanes that share a chunk column, and the row sums over all lanes.
+  #pragma unroll
+    for (int e = 0; e < 8; ++e)
+  #pragma unroll
+      for (int off = CPR; off < 64; off <<= 1) o[e] += __shfl_xor(o[e], off, 64);
+    lsum = wave_sum_dpp(lsum);
+    if (wave >= G) continue;  // padding head
+    if (slot < 0) {
+      if (lane < CPR) {
+        const float inv = 1.f / lsum;
+        float r[8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = o[e] * inv;
+        st16(out + ((size_t)token * Hq + (size_t)kvh * G + hg) * D + cl * 8, pack_chunk<bf16_t>(r));
+      }
+    } else {
+      float* part = ws + (size_t)slot * G * (D + 2);
+      if (lane == 0) {
+        part[hg] = m_run;
+        part[G + hg] = lsum;
+      }
+      if (lane < CPR) {
+        float* dst = part + 2 * G + (size_t)hg * D + cl * 8;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = o[e];
+      }
     }
-  } else {
-    float* part = ws + (size_t)slot * G * (D + 2);
-    if (lane == 0) {
-      part[hg] = m_run;
-      part[G + hg] = lsum;
-    }
-    if (lane < CPR) {
-      float* dst = part + 2 * G + (size_t)hg * D + cl * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = o[e];
-    }
-  }
   }  // items
 }
 
