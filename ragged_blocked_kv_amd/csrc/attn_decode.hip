@@ -524,9 +524,9 @@ void decode_group_kernel(
   }
 }
 
-// Lean grouped decode for bf16 caches over blocks of at least 64 keys: NW (4 or 8)
-// wavefronts of at most 96 registers, one per query head of the kv group (waves past G
-// repeat the last head and write nothing), and one 64-key K/V tile in LDS (32 KB at head
+// Lean grouped decode for bf16 caches over blocks of at least 64 keys, groups of up to
+// four heads: NW = 4 wavefronts of at most 96 registers, one per query head of the kv
+// group (waves past G repeat the last head and write nothing), and one 64-key K/V tile in LDS (32 KB at head
 // dim 128) with nothing else there: the softmax weights reach the P.V lanes through
 // ds_bpermute, which needs no LDS allocation, and the query row sits in scalar registers.
 // The tile is loaded straight from HBM into LDS by all the waves from a uniform block base;
@@ -554,7 +554,8 @@ void decode_lean_kernel(
   constexpr int NLD = TILE_CHUNKS / NT;      // direct loads per thread per K (or V) tile
   constexpr int KPI = 64 / CPR;              // P.V: keys per row group
   constexpr int NI = CPR;                    // P.V: row groups per tile
-  static_assert(TILE_CHUNKS % NT == 0, "loader geometry");
+  // The loader takes one K swizzle per thread: each load must cover a multiple of 16 rows.
+  static_assert(TILE_CHUNKS % NT == 0 && (NT / CPR) % 16 == 0, "loader geometry");
   __shared__ __attribute__((aligned(16))) uint16_t Kt[64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[64 * D];
 
@@ -730,6 +731,233 @@ void decode_lean_kernel(
 
 // claim == nullptr: one workgroup per item.  Otherwise `workgroups` persistent
 // workgroups (at most one per item) drain the list through the counter.
+// Lean decode with two query heads per wavefront, for bf16 groups of 5 to 8 heads over
+// blocks of at least 64 keys: four wavefronts cover up to eight heads, so each K and V
+// chunk a lane reads from LDS serves two heads and a workgroup is half the size of an
+// eight-wave one (four fit on a CU instead of two: more tiles in flight per CU).  The
+// group's query rows sit in LDS (2 KB at head dim 128, read as broadcasts); the tile,
+// the loader, the online softmax (one per head), P.V with the V chunks copied to
+// registers before the barrier that frees the tile, the work items and the claim loop are
+// those of the one-head kernel above, and so is each head's arithmetic and its order.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 2, NW == 4 ? 4 : 2)))
+void decode_lean2_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
+    uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
+    const int32_t* __restrict__ tok2seq, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2,
+    int32_t* __restrict__ claim, int32_t n_items) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
+  constexpr int NT = NW * 64;                // threads
+  constexpr int TILE_CHUNKS = 64 * CPR;      // chunks per K (or V) tile
+  constexpr int NLD = TILE_CHUNKS / NT;      // direct loads per thread per K (or V) tile
+  constexpr int KPI = 64 / CPR;              // P.V: keys per row group
+  constexpr int NI = CPR;                    // P.V: row groups per tile
+  constexpr int NH = 2 * NW;                 // heads the workgroup covers
+  static_assert(TILE_CHUNKS % NT == 0 && NH * CPR <= NT, "loader geometry");
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[NH * D];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  auto next_item = [&]() -> int32_t {
+    __syncthreads();  // every wave is done with the previous item's tile and query rows
+    if (tid == 0) {
+      const uint32_t c = (uint32_t)atomicAdd(claim, 1);
+      Kt[0] = (uint16_t)c;
+      Kt[1] = (uint16_t)(c >> 16);
+    }
+    __syncthreads();
+    const int32_t it = __builtin_amdgcn_readfirstlane((int32_t)(Kt[0] | ((uint32_t)Kt[1] << 16)));
+    __syncthreads();  // read by every wave before the next tile lands there
+    return it;
+  };
+  for (int32_t item = claim ? next_item() : (int32_t)blockIdx.x; item < n_items;
+       item = claim ? next_item() : n_items) {
+    const int4 w = work[item];
+    const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
+    const int32_t seq = tok2seq[token];
+    const int32_t nkeys = pos[token] + 1;
+    const int32_t tiles_total = (nkeys + 63) >> 6;
+    const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
+    const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
+    const int32_t key_end = min(nkeys, t_end * 64);
+    const int32_t* bids = block_ids + block_off[seq];
+    const int bsh = 31 - __builtin_clz(bs);  // block sizes are powers of two
+    const int32_t last_blk = (key_end - 1) >> bsh;
+    const size_t head_stride = (size_t)bs * D;
+    const size_t blk_stride = (size_t)2 * Hkv * head_stride;
+    const size_t v_off = (size_t)Hkv * head_stride;
+    const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
+    // This wave's two heads (uniform); heads past G repeat the last one.
+    const int32_t h0 = __builtin_amdgcn_readfirstlane(min(2 * wave, G - 1));
+    const int32_t h1 = __builtin_amdgcn_readfirstlane(min(2 * wave + 1, G - 1));
+
+    auto kswz = [](int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); };
+    auto fetch_ids = [&](int32_t t, int32_t* ids) { ids[0] = bids[min((t * 64) >> bsh, last_blk)]; };
+    const uint32_t k_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[0]) + wave * 64 * 16);
+    const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vt[0]) + wave * 64 * 16);
+    // Loader lanes: row tid / CPR + i * (NT / CPR) of the tile, chunk tid % CPR.  The K
+    // swizzle depends on the row's low four bits, which change with i when a load covers
+    // fewer than 16 rows (two waves at head dim 128), so it is taken per load.
+    const int ld_r0 = tid / CPR, ld_c = tid % CPR;
+    const uint32_t ld_vc = (uint32_t)ld_c * 16u;
+    auto issue_tile = [&](int32_t t, const int32_t* ids) {
+      const int32_t key0 = t * 64;
+      const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
+      const int32_t rmax = key_end - 1 - key0;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint32_t roff = (uint32_t)min(ld_r0 + i * (NT / CPR), rmax) * (D * 2);
+        const uint32_t ld_kc = (uint32_t)(ld_c ^ kswz(ld_r0 + i * (NT / CPR))) * 16u;
+        const uint32_t off = i * NT * 16;
+        load_lds16_nt_s(base, roff + ld_kc, k_dst0 + off);
+        load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + off);
+      }
+    };
+
+    // The group's query rows into LDS (head slots past G repeat the last head); made
+    // visible by the barrier at the top of the first tile.
+    if (tid < NH * CPR) {
+      const int hq = min(tid / CPR, G - 1), c = tid % CPR;
+      const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + hq) * D;
+      *(u32x4*)(Qs + tid * 8) = ld16(qrow + c * 8);
+    }
+    int32_t ids[1];
+    fetch_ids(t_begin, ids);
+    issue_tile(t_begin, ids);
+    fetch_ids(min(t_begin + 1, t_end - 1), ids);
+
+    float m_run[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f}, o[2][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[0][e] = o[1][e] = 0.f;
+    const int cl = lane % CPR, kg = lane / CPR;  // P.V: chunk column and key sub-row
+    uint32_t krow = (uint32_t)(lane * CPR + kswz(lane)) * 16u;
+    uint32_t vcol = (uint32_t)(kg * CPR + cl) * 16u;
+    uint32_t pidx = (uint32_t)kg * 4u;
+    const u32x4* q0 = (const u32x4*)(Qs + h0 * D);
+    const u32x4* q1 = (const u32x4*)(Qs + h1 * D);
+
+    for (int32_t tt = t_begin; tt < t_end; ++tt) {
+      wait_vmcnt<0>();  // this wave's share of tile tt (and its query-row load)
+      __syncthreads();  // every wave's share
+      const int32_t key0 = tt * 64;
+      asm volatile("" : "+v"(krow), "+v"(vcol), "+v"(pidx));
+
+      // Scores of both heads: lane = key, each K chunk read once.
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPR; ++c) {
+        const u32x4 kc = *(const u32x4*)((const char*)Kt + (krow ^ (16u * c)));
+        s0 = dot_chunk(q0[c], kc, s0, bf16_t{});
+        s1 = dot_chunk(q1[c], kc, s1, bf16_t{});
+      }
+      const bool valid = key0 + lane < key_end;
+      float pe[2], alpha[2];
+      {
+        const float sc0 = valid ? s0 * scale_log2 : -INFINITY;
+        const float sc1 = valid ? s1 * scale_log2 : -INFINITY;
+        const float mn0 = fmaxf(m_run[0], wave_max_dpp(sc0));
+        const float mn1 = fmaxf(m_run[1], wave_max_dpp(sc1));
+        alpha[0] = __builtin_amdgcn_exp2f(m_run[0] - mn0);
+        alpha[1] = __builtin_amdgcn_exp2f(m_run[1] - mn1);
+        pe[0] = __builtin_amdgcn_exp2f(sc0 - mn0);
+        pe[1] = __builtin_amdgcn_exp2f(sc1 - mn1);
+        m_run[0] = mn0;
+        m_run[1] = mn1;
+        lsum[0] = lsum[0] * alpha[0] + pe[0];
+        lsum[1] = lsum[1] * alpha[1] + pe[1];
+      }
+      u32x4 vr[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        vr[i] = *(const u32x4*)((const char*)Vt + vcol + i * (KPI * CPR * 16));
+      if (tt + 1 < t_end) {
+        __syncthreads();  // every wave is done with the tile before it is overwritten
+        issue_tile(tt + 1, ids);
+        fetch_ids(min(tt + 2, t_end - 1), ids);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[0][e] *= alpha[0];
+        o[1][e] *= alpha[1];
+      }
+      const int pb0 = __float_as_int(pe[0]), pb1 = __float_as_int(pe[1]);
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        const int ia = (int)(pidx + i * KPI * 4), ib = (int)(pidx + (i + 1) * KPI * 4);
+        const bf16x2v pp0 = as_bf16x2(pack_bf16x2(__int_as_float(__builtin_amdgcn_ds_bpermute(ia, pb0)),
+                                                  __int_as_float(__builtin_amdgcn_ds_bpermute(ib, pb0))));
+        const bf16x2v pp1 = as_bf16x2(pack_bf16x2(__int_as_float(__builtin_amdgcn_ds_bpermute(ia, pb1)),
+                                                  __int_as_float(__builtin_amdgcn_ds_bpermute(ib, pb1))));
+        const uint32_t aw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        const uint32_t bw[4] = {vr[i + 1].x, vr[i + 1].y, vr[i + 1].z, vr[i + 1].w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const bf16x2v lo = as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x05040100u));
+          const bf16x2v hi = as_bf16x2(__builtin_amdgcn_perm(bw[jj], aw[jj], 0x07060302u));
+          o[0][2 * jj] = __builtin_amdgcn_fdot2_f32_bf16(pp0, lo, o[0][2 * jj], false);
+          o[0][2 * jj + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp0, hi, o[0][2 * jj + 1], false);
+          o[1][2 * jj] = __builtin_amdgcn_fdot2_f32_bf16(pp1, lo, o[1][2 * jj], false);
+          o[1][2 * jj + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp1, hi, o[1][2 * jj + 1], false);
+        }
+      }
+    }
+
+    // Reduce over the lanes that share a chunk column, and the row sums over all lanes.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int off = CPR; off < 64; off <<= 1) o[h][e] += __shfl_xor(o[h][e], off, 64);
+      lsum[h] = wave_sum_dpp(lsum[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int32_t hh = h == 0 ? h0 : h1;
+      if (2 * wave + h >= G) continue;  // padding head
+      if (slot < 0) {
+        if (lane < CPR) {
+          const float inv = 1.f / lsum[h];
+          float r[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r[e] = o[h][e] * inv;
+          st16(out + ((size_t)token * Hq + (size_t)kvh * G + hh) * D + cl * 8, pack_chunk<bf16_t>(r));
+        }
+      } else {
+        float* part = ws + (size_t)slot * G * (D + 2);
+        if (lane == 0) {
+          part[hh] = m_run[h];
+          part[G + hh] = lsum[h];
+        }
+        if (lane < CPR) {
+          float* dst = part + 2 * G + (size_t)hh * D + cl * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dst[e] = o[h][e];
+        }
+      }
+    }
+  }  // items
+}
+
+template <int D, int NW>
+hipError_t launch_lean2(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                        const void* pool, void* out, float* ws, hipStream_t stream,
+                        int32_t* claim = nullptr, int32_t workgroups = 0) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  const int G = s.n_q_heads / s.n_kv_heads;
+  const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
+  hipLaunchKernelGGL((decode_lean2_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream,
+                     (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
+                     (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
+                     b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
+                     scale_log2, claim, b.n_decode_items);
+  return hipGetLastError();
+}
+
 template <int D, int NW>
 hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                        const void* pool, void* out, float* ws, hipStream_t stream,
@@ -794,10 +1022,11 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
                     void* out, float* ws, hipStream_t stream) {
   const int G = s.n_q_heads / s.n_kv_heads;
   if constexpr (sizeof(T) == 2) {
-    // bf16 groups of up to 8 heads over blocks of 64+ keys: one wave per head, one tile.
+    // bf16 groups of up to 8 heads over blocks of 64+ keys: one K/V tile per workgroup,
+    // one wave per head up to 4 heads, two heads per wave for 5-8.
     if (decode_lean_ok(s))
       return G <= 4 ? launch_lean<D, 4>(s, b, qkv, pool, out, ws, stream)
-                    : launch_lean<D, 8>(s, b, qkv, pool, out, ws, stream);
+                    : launch_lean2<D, 4>(s, b, qkv, pool, out, ws, stream);
     // Other bf16 groups of 5 or more heads: one wave per head over two LDS tile stages.
     if (decode_grouped(s))
       return G <= 8 ? launch_group<D, 8>(s, b, qkv, pool, out, ws, stream)
@@ -823,9 +1052,9 @@ hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, co
   const bool g4 = s.n_q_heads / s.n_kv_heads <= 4;
   if (s.head_dim == 128)
     return g4 ? launch_lean<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
-              : launch_lean<128, 8>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+              : launch_lean2<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
   return g4 ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
-            : launch_lean<64, 8>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+            : launch_lean2<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
 }
 
 hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,

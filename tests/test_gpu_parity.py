@@ -149,9 +149,9 @@ def test_tiny_f32_workload():
 @pytest.mark.parametrize("seed", range(17))
 def test_random_small_batches(seed):
     # Every decode kernel instantiation appears: per-wave (float32; bf16 G <= 4 over blocks
-    # under 64 keys), lean 4-wave (bf16 G <= 4, blocks >= 64; d 64 and 128), lean 8-wave
-    # (bf16 G 5..8, blocks >= 64; d 64 and 128) and grouped (bf16 G 9..16, or G 5..8 over
-    # blocks under 64 keys).
+    # under 64 keys), lean one head per wave (bf16 G <= 4, blocks >= 64; d 64 and 128),
+    # lean two heads per wave (bf16 G 5..8, blocks >= 64; d 64 and 128) and grouped (bf16
+    # G 9..16, or G 5..8 over blocks under 64 keys).
     combos = [  # dtype, Hq, Hkv, d, bs
         ("bf16", 4, 2, 64, 16), ("bf16", 8, 8, 128, 64), ("f32", 4, 1, 64, 32),
         ("bf16", 14, 2, 128, 32), ("f32", 8, 4, 128, 128), ("bf16", 16, 1, 64, 128),
