@@ -559,21 +559,28 @@ def main():
     # The timed step: the same work with the prefill and the decodes sharing the chip
     # (ragged_blocked_attention_concurrent, bit-identical output), bracketed by
     # synchronisations.
-    def step_concurrent():
+    def step_concurrent(ev=None):
         eng.rebuild(stream=stream)
         eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
         eng.attention_concurrent(qkv, pool, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)  # after the join: both streams' work is done
 
     wall = wall_serial
+    two_stream = None
     if not args.serial_only:
         for _ in range(args.warmup):
             step_concurrent()
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            step_concurrent()
+            step_concurrent(cev[k])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        two_stream = np.array([cev[k][0].elapsed_time(cev[k][1]) for k in range(args.steps)])
 
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
@@ -651,6 +658,14 @@ def main():
         "step_us_p10_p50_p90": [round(float(np.percentile(step_ev, q)) * 1e3, 1)
                                 for q in (10, 50, 90)],
         "finalize_call_us": finalize_us,
+        "attention_two_stream": None if two_stream is None else {
+            "us_p10_p50_p90": [round(float(np.percentile(two_stream, q)) * 1e3, 1)
+                               for q in (10, 50, 90)],
+            "tokens_per_s": wl.T / (float(np.median(two_stream)) * 1e-3),
+            # every K/V row and Q/output of the batch once, over the two-stream attention time
+            "hbm_frac_attention": work["attention_bytes"] / (float(np.median(two_stream)) * 1e-3)
+                                  / 1e9 / HBM_PEAK_GBS,
+        },
         "serial_step": {"ms_per_step": wall_serial * 1e3 / args.steps,
                         "tokens_per_s": wl.T * args.steps / wall_serial,
                         "step": "the same phases one after another on one stream, with HIP "
