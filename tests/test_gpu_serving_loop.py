@@ -243,15 +243,19 @@ SPLITFUSE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("two_stream", [False, True], ids=["serial", "two_stream"])
 @pytest.mark.parametrize("case", SPLITFUSE_CASES, ids=lambda c: c.name)
-def test_splitfuse_loop_matches_oracle(case):
+def test_splitfuse_loop_matches_oracle(case, two_stream):
     """The same loop with batches composed by Dynamic SplitFuse on both ledgers (the
     composed batches must be identical): decodes first, then prompts in arrival order
-    cut to fill the token budget, the rest of a prompt continuing in later passes."""
+    cut to fill the token budget, the rest of a prompt continuing in later passes.  With
+    two_stream the attention is ragged_blocked_attention_concurrent (for the bf16 cases
+    over 64-key blocks: persistent decodes beside the prefill, on batches whose mix of
+    chunks and decodes changes every pass, some with no chunk at all)."""
     from ragged_blocked_kv_amd.runtime import Engine
     from ragged_blocked_kv_amd.state import StateManager
 
-    print(f"splitfuse loop {case.name}", flush=True)
+    print(f"splitfuse loop {case.name} two_stream={two_stream}", flush=True)
     dev = torch.device("cuda:0")
     c = case
     max_context = c.max_prompt + c.max_gen + 1
@@ -320,7 +324,10 @@ def test_splitfuse_loop_matches_oracle(case):
         out = torch.empty((T, c.n_q_heads, c.head_dim), dtype=eng.torch_dtype, device=dev)
         eng.finalize_state(nat)
         eng.append_rotary(qkv, pool, 1e4)
-        eng.attention(qkv, pool, out)
+        if two_stream:
+            eng.attention_concurrent(qkv, pool, out)
+        else:
+            eng.attention(qkv, pool, out)
         torch.cuda.synchronize()
         want = loop.step(uids, n_new, _storage_numpy(qkv_cpu, c.dtype))
         err = float(np.max(np.abs(out.float().cpu().numpy().astype(np.float64) - want)))
