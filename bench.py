@@ -262,7 +262,8 @@ def serving_leg(wl, eng, qkv, pool, out, stream, passes=12, warm=3):
     """A Dynamic SplitFuse serving loop on the bench's shapes, end to end per pass:
     compose the batch on the native ledger (the decodes of the batch's single-token
     sequences first, then a seeded queue of prompts of 256..4096 tokens cut to fill the
-    8192-token budget), put, finalize from the ledger, rotary append, attention,
+    8192-token budget), put, finalize from the ledger, rotary append, attention (the
+    two-stream call),
     synchronize (a serving loop needs the pass's output before composing the next one)
     and post_forward.  Finished prompts are flushed; decodes run on.  Times are medians
     over the timed passes."""
@@ -302,7 +303,7 @@ def serving_leg(wl, eng, qkv, pool, out, stream, passes=12, warm=3):
         t1 = time.perf_counter()
         ev0.record(stream)
         eng.append_rotary(qkv, pool, wl.rope_base, stream=stream, batch=b)
-        eng.attention(qkv, pool, out, stream=stream, batch=b)
+        eng.attention_concurrent(qkv, pool, out, stream=stream, batch=b)
         ev1.record(stream)
         torch.cuda.synchronize()
         t2 = time.perf_counter()
