@@ -167,13 +167,26 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[0][0]) + (wave & 3) * 64 * 16);
   auto issue_loads = [&](int32_t t, const int32_t* ids, int buf) {
     const uint32_t kd = k_dst0 + buf * TILE_BYTES, vd = v_dst0 + buf * TILE_BYTES;
-    if (bs >= 64 && t * 64 + 63 < n_keys) {
-      // The whole tile sits in one block: one uniform base, fixed per-thread offsets.
+    if (bs >= 64) {
+      // The tile sits in one block: a uniform base in scalar registers and 32-bit
+      // per-thread offsets (measured 4% faster than 64-bit per-lane addresses).  Rows past
+      // the end of a partial last tile load its last key (never read unmasked).
       const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)((t * 64) % bs) * D;
+      const uint16_t* vbase = base + v_off;
+      if (t * 64 + 63 < n_keys) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        load_lds16(base + i * ROWS_PER_LD * D + k_src, kd + i * LOADERS * 16);
-        load_lds16(base + v_off + i * ROWS_PER_LD * D + v_src, vd + i * LOADERS * 16);
+        for (int i = 0; i < NLD; ++i) {
+          load_lds16_s(base, (uint32_t)(i * ROWS_PER_LD * D + k_src) * 2u, kd + i * LOADERS * 16);
+          load_lds16_s(vbase, (uint32_t)(i * ROWS_PER_LD * D + v_src) * 2u, vd + i * LOADERS * 16);
+        }
+      } else {
+        const int32_t rmax = n_keys - 1 - t * 64;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int32_t shift = (min(i * ROWS_PER_LD + lrow, rmax) - lrow) * D;
+          load_lds16_s(base, (uint32_t)(shift + k_src) * 2u, kd + i * LOADERS * 16);
+          load_lds16_s(vbase, (uint32_t)(shift + v_src) * 2u, vd + i * LOADERS * 16);
+        }
       }
       return;
     }

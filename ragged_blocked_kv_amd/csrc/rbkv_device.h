@@ -130,8 +130,12 @@ __device__ __forceinline__ void load_lds16_nt(const void* src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
-// The same from a uniform 64-bit base (scalar registers) plus a 32-bit lane offset, which
-// keeps one vector register per load address instead of two.
+// From a uniform 64-bit base (scalar registers) plus a 32-bit lane offset, which keeps one
+// vector register per load address instead of two.
+__device__ __forceinline__ void load_lds16_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+// The same with the non-temporal cache policy.
 __device__ __forceinline__ void load_lds16_nt_s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
