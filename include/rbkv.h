@@ -245,7 +245,9 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
  * fork and join use two caller-owned events (hipEvent_t as void*, created by the
  * caller, e.g. with hipEventDisableTiming): fork_event is recorded on `stream` and
  * waited on by `side_stream`; join_event is recorded on `side_stream` and waited on by
- * `stream`.  Both streams must be of the current device and must differ.  With no
+ * `stream` (on the persistent-decode path twice: after the counter reset, which runs on
+ * `side_stream`, before the main stream's own decode launch, and at the end).  Both
+ * streams must be of the current device and must differ.  With no
  * prefill or no decode work the call runs like ragged_blocked_attention on `stream`
  * alone and leaves the events unused.  Graph-capturable like the rest (the standard
  * event fork/join).  Errors: as ragged_blocked_attention, plus INVALID_ARG (NULL

@@ -575,12 +575,18 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
   }
   int32_t* claim = (int32_t*)(ws + claim_offset(s, b));
   float* partials = (float*)ws;
-  bool ok = launch_decode_claim_reset(claim, hs) == hipSuccess &&
-            hipEventRecord(fork, hs) == hipSuccess &&
+  // The counter reset runs on the side stream ahead of the side decodes, so the prefill
+  // starts on the main stream at once; the join event is recorded right after the reset
+  // and the main stream waits for that record before its own decode launch (long done by
+  // the time the prefill ends), then recorded again at the end for the final join.
+  bool ok = hipEventRecord(fork, hs) == hipSuccess &&
             hipStreamWaitEvent(hside, fork, 0) == hipSuccess &&
+            launch_decode_claim_reset(claim, hside) == hipSuccess &&
+            hipEventRecord(join, hside) == hipSuccess &&
             launch_prefill(s, b, qkv, kv_pool, out, hs) == hipSuccess &&
             launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
                                      OVERLAP_SIDE_WG_PER_CU * n_cu, hside) == hipSuccess &&
+            hipStreamWaitEvent(hs, join, 0) == hipSuccess &&
             launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
                                      OVERLAP_MAIN_WG_PER_CU * n_cu, hs) == hipSuccess;
   // Join whatever was launched, so the caller's stream never runs ahead of the side work.
