@@ -46,8 +46,8 @@ __global__ __launch_bounds__(AP_THREADS) void append_rotary_kernel(
   const int64_t blk = block_ids[block_off[i] + p / bs];
   const int32_t slot = p % bs;
   T* row = qkv + (size_t)t * (Hq + 2 * Hkv) * D;
-  const size_t kbase = (size_t)((blk * 2 + 0) * Hkv) * bs * D + (size_t)slot * D;
-  const size_t vbase = (size_t)((blk * 2 + 1) * Hkv) * bs * D + (size_t)slot * D;
+  const size_t kbase = ((size_t)blk * 2 + 0) * Hkv * bs * D + (size_t)slot * D;
+  const size_t vbase = ((size_t)blk * 2 + 1) * Hkv * bs * D + (size_t)slot * D;
   const size_t head_stride = (size_t)bs * D;
 
   // Q heads (rotated in place) and K heads (rotated into the pool).

@@ -529,18 +529,22 @@ void decode_group_kernel(
 // group (waves past G repeat the last head and write nothing), and one 64-key K/V tile in LDS (32 KB at head
 // dim 128) with nothing else there: the softmax weights reach the P.V lanes through
 // ds_bpermute, which needs no LDS allocation, and the query row sits in scalar registers.
-// The tile is loaded straight from HBM into LDS by all the waves from a uniform block base;
-// each lane copies its V chunks to registers before the barrier that frees the tile, so
-// the next tile's loads fly while P.V is summed, and the other workgroups on the CU (five
-// four-wave ones fit) hide the rest of the latency.  Arithmetic and order are those of the
+// The tile is loaded straight from HBM into LDS by all the waves from a uniform block base.
+// ST = 1: each lane copies its V chunks to registers before the barrier that frees the
+// tile, so the next tile's loads fly while P.V is summed, and the other workgroups on the
+// CU (five four-wave ones fit) hide the rest of the latency.  ST = 2: two tile stages, one
+// barrier per tile, after which the next tile goes into the other stage at once, so every
+// workgroup always has a tile in flight; two workgroups share a CU at head dim 128 (random
+// 16 KiB tiles stream fastest with about two in flight per CU: five one-stage workgroups
+// per CU read 8% slower in a load-only probe).  Arithmetic and order are those of the
 // kernels above (same results, bit for bit).  Work items, split-K partition and partial
 // layout are those of the kernels above; with a claim counter the workgroups are
 // persistent and take items from it.  (A four-wave workgroup would also fit in what a
 // prefill workgroup leaves free on its CU, two waves of 208 registers per SIMD and 128 KB
 // of LDS; measured, sharing CUs that way was slower than letting the two kernels divide
 // the CUs between them.)
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5, 5)))
+template <int D, int NW, int ST>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ST == 1 ? 5 : 2, ST == 1 ? 5 : 2)))
 void decode_lean_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
@@ -556,8 +560,10 @@ void decode_lean_kernel(
   constexpr int NI = CPR;                    // P.V: row groups per tile
   // The loader takes one K swizzle per thread: each load must cover a multiple of 16 rows.
   static_assert(TILE_CHUNKS % NT == 0 && (NT / CPR) % 16 == 0, "loader geometry");
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[64 * D];
+  static_assert(ST == 1 || ST == 2, "stages");
+  constexpr uint32_t TILE_BYTES = 64 * D * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[ST * 64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[ST * 64 * D];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // With a claim counter the workgroup is persistent: it takes item after item from the
@@ -609,7 +615,7 @@ void decode_lean_kernel(
     const uint32_t ld_kc = (uint32_t)(ld_c ^ kswz(ld_r0)) * 16u, ld_vc = (uint32_t)ld_c * 16u;
     // Blocks hold at least 64 keys, so a tile lies in one block: a uniform base and 32-bit
     // lane offsets.  Rows past the end of the split load its last key (never read unmasked).
-    auto issue_tile = [&](int32_t t, const int32_t* ids) {
+    auto issue_tile = [&](int32_t t, const int32_t* ids, uint32_t stage_off) {
       const int32_t key0 = t * 64;
       const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
       const int32_t rmax = key_end - 1 - key0;
@@ -617,8 +623,8 @@ void decode_lean_kernel(
       for (int i = 0; i < NLD; ++i) {
         const uint32_t roff = (uint32_t)min(ld_r0 + i * (NT / CPR), rmax) * (D * 2);
         const uint32_t off = i * NT * 16;
-        load_lds16_nt_s(base, roff + ld_kc, k_dst0 + off);
-        load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + off);
+        load_lds16_nt_s(base, roff + ld_kc, k_dst0 + stage_off + off);
+        load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + stage_off + off);
       }
     };
 
@@ -630,7 +636,7 @@ void decode_lean_kernel(
     }
     int32_t ids[1];
     fetch_ids(t_begin, ids);
-    issue_tile(t_begin, ids);
+    issue_tile(t_begin, ids, 0);
     fetch_ids(min(t_begin + 1, t_end - 1), ids);
 
     float m_run = -INFINITY, lsum = 0.f, o[8];
@@ -649,15 +655,23 @@ void decode_lean_kernel(
 
     for (int32_t tt = t_begin; tt < t_end; ++tt) {
       wait_vmcnt<0>();  // this wave's share of tile tt
-      __syncthreads();  // every wave's share
+      __syncthreads();  // every wave's share (two stages: and every wave is done with tile tt-1)
+      const uint32_t soff = ((tt - t_begin) & (ST - 1)) * TILE_BYTES;  // this tile's stage
+      if constexpr (ST == 2) {
+        if (tt + 1 < t_end) {
+          issue_tile(tt + 1, ids, soff ^ TILE_BYTES);
+          fetch_ids(min(tt + 2, t_end - 1), ids);
+        }
+      }
       const int32_t key0 = tt * 64;
       asm volatile("" : "+v"(krow), "+v"(vcol), "+v"(pidx));
+      const uint32_t kr = krow + soff, vc = vcol + soff;
 
       // Scores: lane = key.
       float s = 0.f;
   #pragma unroll
       for (int c = 0; c < CPR; ++c)
-        s = dot_chunk(q[c], *(const u32x4*)((const char*)Kt + (krow ^ (16u * c))), s, bf16_t{});
+        s = dot_chunk(q[c], *(const u32x4*)((const char*)Kt + (kr ^ (16u * c))), s, bf16_t{});
       const float sc = key0 + lane < key_end ? s * scale_log2 : -INFINITY;
       const float mn = fmaxf(m_run, wave_max_dpp(sc));
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
@@ -672,11 +686,13 @@ void decode_lean_kernel(
       u32x4 vr[NI];
   #pragma unroll
       for (int i = 0; i < NI; ++i)
-        vr[i] = *(const u32x4*)((const char*)Vt + vcol + i * (KPI * CPR * 16));
-      if (tt + 1 < t_end) {
-        __syncthreads();  // every wave is done with the tile before it is overwritten
-        issue_tile(tt + 1, ids);
-        fetch_ids(min(tt + 2, t_end - 1), ids);
+        vr[i] = *(const u32x4*)((const char*)Vt + vc + i * (KPI * CPR * 16));
+      if constexpr (ST == 1) {
+        if (tt + 1 < t_end) {
+          __syncthreads();  // every wave is done with the tile before it is overwritten
+          issue_tile(tt + 1, ids, 0);
+          fetch_ids(min(tt + 2, t_end - 1), ids);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
@@ -965,7 +981,14 @@ hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int G = s.n_q_heads / s.n_kv_heads;
   const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
-  hipLaunchKernelGGL((decode_lean_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream,
+  // One workgroup per item at head dim 128 and groups of 2-4 heads: two tile stages (64 KB,
+  // two workgroups per CU), so a tile load is always in flight.  Single-head groups, whose
+  // items are whole sequences of mixed length, keep five one-stage workgroups per CU (with
+  // two per CU their tail varied run to run), and so do the persistent workgroups of the
+  // two-stream call and head dim 64.
+  auto kern = (!claim && D == 128 && G >= 2) ? decode_lean_kernel<D, NW, 2>
+                                             : decode_lean_kernel<D, NW, 1>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
                      (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
                      b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
