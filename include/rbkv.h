@@ -237,7 +237,8 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
  * identical (bit for bit) to ragged_blocked_attention.  For bf16 groups of at most four
  * heads over blocks of 64+ keys the decodes run as persistent workgroups taking items
  * from a counter in the workspace (reset by the call): two per CU start beside the
- * prefill, and four per CU more join on `stream` once the prefill is done, so the chip
+ * prefill, and more join on `stream` once the prefill is done (two per CU with two LDS
+ * tile stages each at head dim 128 and groups of 2-4 heads, else four), so the chip
  * is shared between the phases rather than split by kernel boundaries (about 10% less
  * time than the serial call on the full-budget and SplitFuse batches).  Other shapes
  * gain only where one phase leaves CUs idle.  Calls sharing a workspace must be ordered

@@ -557,12 +557,16 @@ namespace {
 
 // The two-stream call for lean-decode shapes: persistent decode workgroups, two per CU,
 // start beside the prefill on the side stream and share the chip with it; once the
-// prefill is done a second launch of four per CU on the main stream joins them.  Both take
-// items from one counter, so they finish together whatever the split of the work.  (Sizes
-// measured on the full-budget and SplitFuse batches: one per CU beside the prefill, or
-// more than three, was slower; the second launch's size matters within 1-2%.)
+// prefill is done a second launch on the main stream joins them: four one-stage
+// workgroups per CU, or, for head dim 128 and groups of 2-4 heads, two of the two-stage
+// form (no prefill workgroup is left to share a CU with; SplitFuse batch 381 -> 377 us,
+// full-budget batch equal within 1%).  Both take items from one counter, so they finish
+// together whatever the split of the work.  (Sizes measured on the full-budget and
+// SplitFuse batches: one per CU beside the prefill, or more than three, was slower; the
+// second launch's size matters within 1-2%.)
 constexpr int OVERLAP_SIDE_WG_PER_CU = 2;
 constexpr int OVERLAP_MAIN_WG_PER_CU = 4;
+constexpr int OVERLAP_MAIN_WG_PER_CU_2ST = 2;
 rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                  const void* kv_pool, void* out, char* ws, hipStream_t hs,
                                  hipStream_t hside, hipEvent_t fork, hipEvent_t join) {
@@ -575,6 +579,8 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
   }
   int32_t* claim = (int32_t*)(ws + claim_offset(s, b));
   float* partials = (float*)ws;
+  const bool two_stage = s.head_dim == 128 && s.n_q_heads / s.n_kv_heads >= 2 &&
+                         s.n_q_heads / s.n_kv_heads <= 4;
   // The counter reset runs on the side stream ahead of the side decodes, so the prefill
   // starts on the main stream at once; the join event is recorded right after the reset
   // and the main stream waits for that record before its own decode launch (long done by
@@ -585,10 +591,12 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
             hipEventRecord(join, hside) == hipSuccess &&
             launch_prefill(s, b, qkv, kv_pool, out, hs) == hipSuccess &&
             launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
-                                     OVERLAP_SIDE_WG_PER_CU * n_cu, hside) == hipSuccess &&
+                                     OVERLAP_SIDE_WG_PER_CU * n_cu, hside, 1) == hipSuccess &&
             hipStreamWaitEvent(hs, join, 0) == hipSuccess &&
             launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
-                                     OVERLAP_MAIN_WG_PER_CU * n_cu, hs) == hipSuccess;
+                                     (two_stage ? OVERLAP_MAIN_WG_PER_CU_2ST
+                                                : OVERLAP_MAIN_WG_PER_CU) * n_cu,
+                                     hs, two_stage ? 2 : 1) == hipSuccess;
   // Join whatever was launched, so the caller's stream never runs ahead of the side work.
   const bool joined = hipEventRecord(join, hside) == hipSuccess &&
                       hipStreamWaitEvent(hs, join, 0) == hipSuccess;

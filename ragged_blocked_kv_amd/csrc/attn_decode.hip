@@ -977,7 +977,7 @@ hipError_t launch_lean2(const rbkv_shape& s, const rbkv_batch& b, const void* qk
 template <int D, int NW>
 hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                        const void* pool, void* out, float* ws, hipStream_t stream,
-                       int32_t* claim = nullptr, int32_t workgroups = 0) {
+                       int32_t* claim = nullptr, int32_t workgroups = 0, int stages = 0) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int G = s.n_q_heads / s.n_kv_heads;
   const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
@@ -986,8 +986,8 @@ hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv
   // items are whole sequences of mixed length, keep five one-stage workgroups per CU (with
   // two per CU their tail varied run to run), and so do the persistent workgroups of the
   // two-stream call and head dim 64.
-  auto kern = (!claim && D == 128 && G >= 2) ? decode_lean_kernel<D, NW, 2>
-                                             : decode_lean_kernel<D, NW, 1>;
+  if (stages == 0) stages = (!claim && D == 128 && G >= 2) ? 2 : 1;
+  auto kern = stages == 2 ? decode_lean_kernel<D, NW, 2> : decode_lean_kernel<D, NW, 1>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
                      (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
@@ -1071,12 +1071,12 @@ hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream) {
 
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
-                                    int32_t workgroups, hipStream_t stream) {
+                                    int32_t workgroups, hipStream_t stream, int stages) {
   const bool g4 = s.n_q_heads / s.n_kv_heads <= 4;
   if (s.head_dim == 128)
-    return g4 ? launch_lean<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+    return g4 ? launch_lean<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups, stages)
               : launch_lean2<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
-  return g4 ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+  return g4 ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups, stages)
             : launch_lean2<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
 }
 

@@ -150,10 +150,11 @@ hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* q
 
 // The lean decode as persistent workgroups draining the decode list through a device
 // counter (decode_lean_ok shapes only); the counter must be zero when the first of the
-// launches sharing it starts (launch_decode_claim_reset).
+// launches sharing it starts (launch_decode_claim_reset).  stages: LDS tile stages per
+// workgroup, 1 or 2, for groups of up to four heads (larger groups have one form).
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
-                                    int32_t workgroups, hipStream_t stream);
+                                    int32_t workgroups, hipStream_t stream, int stages);
 hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream);
 
 hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
