@@ -146,10 +146,11 @@ def test_tiny_f32_workload():
     run_full(wl, rope_base=0.0)
 
 
-@pytest.mark.parametrize("seed", range(17))
+@pytest.mark.parametrize("seed", range(19))
 def test_random_small_batches(seed):
     # Every decode kernel instantiation appears: per-wave (float32; bf16 G <= 4 over blocks
-    # under 64 keys), lean one head per wave (bf16 G <= 4, blocks >= 64; d 64 and 128),
+    # under 64 keys), lean one head per wave (bf16 G <= 4, blocks >= 64; d 64 and 128; its
+    # two-stage form for G 2..4 at d 128: seeds 9, 17, 18),
     # lean two heads per wave (bf16 G 5..8, blocks >= 64; d 64 and 128) and grouped (bf16
     # G 9..16, or G 5..8 over blocks under 64 keys).
     combos = [  # dtype, Hq, Hkv, d, bs
@@ -158,7 +159,8 @@ def test_random_small_batches(seed):
         ("bf16", 8, 2, 128, 16), ("f32", 2, 2, 64, 64), ("bf16", 6, 2, 64, 64),
         ("bf16", 32, 8, 128, 64), ("f32", 4, 4, 128, 16), ("bf16", 3, 1, 128, 32),
         ("bf16", 16, 2, 128, 64), ("bf16", 24, 3, 64, 16), ("bf16", 12, 2, 64, 128),
-        ("bf16", 40, 8, 128, 128), ("bf16", 7, 1, 64, 64),
+        ("bf16", 40, 8, 128, 128), ("bf16", 7, 1, 64, 64), ("bf16", 4, 2, 128, 128),
+        ("bf16", 6, 2, 128, 64),
     ]
     dt, Hq, Hkv, d, bs = combos[seed]
     wl = W.random_workload(seed, dtype=dt, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
