@@ -1,6 +1,6 @@
 // Device metadata of one ragged batch, built from the staged per-sequence counts:
 // cu_seqlens, kv_len, block_offsets, per-token owner and absolute position, and the three
-// attention work lists.  Every 1024-thread workgroup plans all sequences and scans the
+// attention work lists (decode items with every whole split ahead of the shorter ones).  Every 1024-thread workgroup plans all sequences and scans the
 // counts itself (a few microseconds, cheaper than a second launch or a grid-wide wait),
 // then writes the records of its own share of the sequences.  ("DeepSpeed Inference v2
 // source tour", section "Ragged batches: packing a whole server into four tensors":
@@ -11,7 +11,8 @@ namespace rbkv {
 namespace {
 
 constexpr int MB_THREADS = 1024;
-constexpr int N_SCANS = 6;  // n_new, blocks, decode items, prefill items, partials, combines
+// n_new, blocks, decode items, prefill items, partials, combines, short decode items
+constexpr int N_SCANS = 7;
 
 // Exclusive prefix sum of vals[0..S) into out[0..S] (out[S] = total) by one wavefront:
 // each lane sums a contiguous run, the 64 run totals are scanned across the wave, then
@@ -65,6 +66,10 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
     vals[3][i] = p.pre_items;
     vals[4][i] = p.partials;
     vals[5][i] = p.comb_items;
+    // A decode sequence's items shorter than a whole split: its last split when that is
+    // partial (which is the whole sequence when it has one split).
+    vals[6][i] = (n == 1 && (int32_t)cdiv64((int64_t)s + 1, KT) - (p.nsplit - 1) * split < split)
+                     ? Hkv : 0;
     s_seen[i] = s;
     s_nsplit[i] = p.nsplit;
     s_pwork[i] = p.pre_items > 0 ? (long long)prefill_work_proxy(n, s, qtt) : -1;
@@ -79,6 +84,11 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
   const int32_t* s_dec = offs[2];
   const int32_t* s_part = offs[4];
   const int32_t* s_comb = offs[5];
+  const int32_t* s_short = offs[6];
+  // Decode items: every whole split first, in sequence order, then the shorter items, so
+  // that workgroups taking items in list order (one per item, or persistent ones from a
+  // counter) end on short ones and finish together.  Partial slots do not move.
+  const int32_t full_total = s_dec[S] - s_short[S];
 
   for (int i = blockIdx.x * MB_THREADS + tid; i <= S; i += gridDim.x * MB_THREADS) {
     cu[i] = s_cu[i];
@@ -100,6 +110,7 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
     const int32_t l_dbase = have ? s_dec[il] : 0, l_nc = have ? vals[5][il] : 0;
     const int32_t l_cbase = have ? s_comb[il] : 0, l_ns = have ? s_nsplit[il] : 1;
     const int32_t l_part = have ? s_part[il] : 0;
+    const int32_t l_sbase = have ? s_short[il] : 0, l_nsh = have ? vals[6][il] : 0;
     const long long l_work = have ? s_pwork[il] : -1;
     const int count = min(64, (S - i0 + GW - 1) / GW);
     for (int k = 0; k < count; ++k) {
@@ -116,22 +127,29 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
       const int32_t ns = __builtin_amdgcn_readlane(l_ns, k);
       const int32_t part = __builtin_amdgcn_readlane(l_part, k);
       if (n == 1) {
+        const int32_t sbase = __builtin_amdgcn_readlane(l_sbase, k);
+        const int32_t hs = __builtin_amdgcn_readlane(l_nsh, k) > 0 ? 1 : 0;
+        const int32_t nfull = ns - hs;  // whole splits per kv head
         for (int local = lane; local < nd; local += 64) {
           int4 r;
+          const int32_t kvh = local / ns, sp = local % ns;
           r.x = base;
-          r.y = local / ns;
-          r.z = local % ns;
+          r.y = kvh;
+          r.z = sp;
           r.w = ns > 1 ? part + local : -1;
-          dec[dbase + local] = r;
+          const int32_t at = (hs && sp == ns - 1) ? full_total + sbase + kvh
+                                                   : dbase - sbase + kvh * nfull + sp;
+          dec[at] = r;
         }
       } else {  // one vector-ALU item per token of a float32 chunk, never split
+        const int32_t sbase = __builtin_amdgcn_readlane(l_sbase, k);
         for (int local = lane; local < nd; local += 64) {
           int4 r;
           r.x = base + local % n;
           r.y = local / n;
           r.z = 0;
           r.w = -1;
-          dec[dbase + local] = r;
+          dec[dbase - sbase + local] = r;
         }
       }
       const int32_t nc = __builtin_amdgcn_readlane(l_nc, k);
