@@ -47,6 +47,7 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
   __shared__ int32_t s_seen[MAX_SEQS_LIMIT];
   __shared__ int32_t s_nsplit[MAX_SEQS_LIMIT];
   __shared__ long long s_pwork[MAX_SEQS_LIMIT];  // chunk work proxy, -1 if not a chunk
+  __shared__ int32_t s_rem[MAX_SEQS_LIMIT];      // tiles of a short decode item, -1 if none
 
   const int tid = threadIdx.x;
   const int32_t S = staging[H_S];
@@ -68,8 +69,10 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
     vals[5][i] = p.comb_items;
     // A decode sequence's items shorter than a whole split: its last split when that is
     // partial (which is the whole sequence when it has one split).
-    vals[6][i] = (n == 1 && (int32_t)cdiv64((int64_t)s + 1, KT) - (p.nsplit - 1) * split < split)
-                     ? Hkv : 0;
+    const int32_t rem = (int32_t)cdiv64((int64_t)s + 1, KT) - (p.nsplit - 1) * split;
+    const bool has_short = n == 1 && rem < split;
+    vals[6][i] = has_short ? Hkv : 0;
+    s_rem[i] = has_short ? rem : -1;
     s_seen[i] = s;
     s_nsplit[i] = p.nsplit;
     s_pwork[i] = p.pre_items > 0 ? (long long)prefill_work_proxy(n, s, qtt) : -1;
@@ -85,9 +88,10 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
   const int32_t* s_part = offs[4];
   const int32_t* s_comb = offs[5];
   const int32_t* s_short = offs[6];
-  // Decode items: every whole split first, in sequence order, then the shorter items, so
-  // that workgroups taking items in list order (one per item, or persistent ones from a
-  // counter) end on short ones and finish together.  Partial slots do not move.
+  // Decode items: every whole split first, in sequence order, then the shorter items,
+  // longest first (ties by sequence), so that workgroups taking items in list order (one
+  // per item, or persistent ones from a counter) end on the shortest ones and finish
+  // together.  Partial slots do not move.
   const int32_t full_total = s_dec[S] - s_short[S];
 
   for (int i = blockIdx.x * MB_THREADS + tid; i <= S; i += gridDim.x * MB_THREADS) {
@@ -130,6 +134,17 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
         const int32_t sbase = __builtin_amdgcn_readlane(l_sbase, k);
         const int32_t hs = __builtin_amdgcn_readlane(l_nsh, k) > 0 ? 1 : 0;
         const int32_t nfull = ns - hs;  // whole splits per kv head
+        // Rank of this sequence's short items among all short items: a ballot count of
+        // the sequences ranked ahead (more tiles, or as many and earlier).
+        int32_t srank = 0;
+        if (hs) {
+          const int32_t ri = s_rem[i];
+          for (int j0 = 0; j0 < S; j0 += 64) {
+            const int j = j0 + lane;
+            const int32_t rj = j < S ? s_rem[j] : -1;
+            srank += __popcll(__ballot(rj > ri || (rj == ri && j < i)));
+          }
+        }
         for (int local = lane; local < nd; local += 64) {
           int4 r;
           const int32_t kvh = local / ns, sp = local % ns;
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(MB_THREADS) void meta_build_kernel(
           r.y = kvh;
           r.z = sp;
           r.w = ns > 1 ? part + local : -1;
-          const int32_t at = (hs && sp == ns - 1) ? full_total + sbase + kvh
+          const int32_t at = (hs && sp == ns - 1) ? full_total + srank * Hkv + kvh
                                                    : dbase - sbase + kvh * nfull + sp;
           dec[at] = r;
         }

@@ -73,15 +73,17 @@ def check_work_coverage(md, b, wl):
             assert t0 < tiles
         cover.setdefault((tok, kvh), []).append(rng)
     # Whole splits come first: once an item shorter than a split of a single-token
-    # sequence appears, only such items follow.
-    seen_short = False
+    # sequence appears, only such items follow, each no longer than the one before.
+    last_short = None
     tok_seq = np.searchsorted(np.asarray(md["cu_seqlens"]), np.arange(T), side="right") - 1
     for tok, kvh, split, slot in md["decode_work"]:
         tiles = -(-(pos[tok] + 1) // 64)
         length = tiles if slot < 0 else min(b.split_tiles, tiles - split * b.split_tiles)
         short = int(wl.n_new[tok_seq[tok]]) == 1 and length < b.split_tiles
-        assert short or not seen_short, (tok, kvh, split, length)
-        seen_short = seen_short or short
+        assert short or last_short is None, (tok, kvh, split, length)
+        if short:
+            assert last_short is None or length <= last_short, (tok, kvh, length, last_short)
+            last_short = length
     cu = md["cu_seqlens"]
     # one record per chunk sequence, ranked by work (longest first); the prefill kernel
     # covers all its query tiles for every kv head
