@@ -981,11 +981,11 @@ hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int G = s.n_q_heads / s.n_kv_heads;
   const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
-  // One workgroup per item at head dim 128 and groups of 2-4 heads: two tile stages (64 KB,
-  // two workgroups per CU), so a tile load is always in flight.  Single-head groups, whose
-  // items are whole sequences of mixed length, keep five one-stage workgroups per CU (with
-  // two per CU their tail varied run to run), and so do the persistent workgroups of the
-  // two-stream call and head dim 64.
+  // stages == 0 (the serial call): one workgroup per item, with two tile stages (64 KB,
+  // two workgroups per CU, so a tile load is always in flight) at head dim 128 and groups
+  // of 2-4 heads.  Single-head groups, whose items are whole sequences of mixed length,
+  // keep five one-stage workgroups per CU (with two per CU their tail varied run to run),
+  // and so does head dim 64.  Persistent launches pass their own choice.
   if (stages == 0) stages = (!claim && D == 128 && G >= 2) ? 2 : 1;
   auto kern = stages == 2 ? decode_lean_kernel<D, NW, 2> : decode_lean_kernel<D, NW, 1>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, stream,
