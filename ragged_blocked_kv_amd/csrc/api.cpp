@@ -105,7 +105,10 @@ bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
 
 // Split size for single-token decodes: about the kernel's target number of items overall.
 int32_t choose_split_tiles(const rbkv_shape& s, int64_t decode_tiles_total) {
-  const int64_t target = decode_grouped(s) ? DECODE_TARGET_ITEMS_GROUPED : DECODE_TARGET_ITEMS;
+  const int64_t target =
+      decode_lean_ok(s) ? (s.n_q_heads / s.n_kv_heads <= 4 ? DECODE_TARGET_ITEMS_LEAN
+                                                          : DECODE_TARGET_ITEMS_LEAN2)
+                        : decode_grouped(s) ? DECODE_TARGET_ITEMS_GROUPED : DECODE_TARGET_ITEMS;
   int64_t st = cdiv64(decode_tiles_total, target);
   if (st < MIN_SPLIT_TILES) st = MIN_SPLIT_TILES;
   if (st > MAX_SPLIT_TILES) st = MAX_SPLIT_TILES;

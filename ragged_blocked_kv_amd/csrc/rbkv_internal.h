@@ -20,9 +20,13 @@ constexpr int MAX_TOKENS_LIMIT = 1 << 20;
 constexpr int MAX_BLOCKS_LIMIT = 1 << 26;
 // Decode split-K sizing: aim for about this many decode work items per batch (one
 // wavefront each), or DECODE_TARGET_ITEMS_GROUPED for the one-wave-per-head kernel
-// (a workgroup each, two resident per CU; finer items trim its tail).
+// (a workgroup each, two resident per CU; finer items trim its tail).  The lean kernels
+// take fewer, longer items (fewer item starts; the list ends on its shortest items):
+// DECODE_TARGET_ITEMS_LEAN for groups of up to four heads, _LEAN2 for five to eight.
 constexpr int64_t DECODE_TARGET_ITEMS = 6144;
 constexpr int64_t DECODE_TARGET_ITEMS_GROUPED = 12288;
+constexpr int64_t DECODE_TARGET_ITEMS_LEAN = 3072;
+constexpr int64_t DECODE_TARGET_ITEMS_LEAN2 = 6144;
 constexpr int MIN_SPLIT_TILES = 4;
 constexpr int MAX_SPLIT_TILES = 64;
 
