@@ -2,10 +2,11 @@
 inputs.  Metadata is compared bit for bit; V placement (and K placement with rotation
 off) bit for bit; rotated Q/K within one storage ulp (bf16) or 1e-5 (float32); pool
 bytes outside the written slots unchanged; attention within max-abs 2e-2 (bf16) or
-1e-4 (float32).  Small batches are compared element by element in full; the five
-full-size workloads (in the launch configuration the benchmark times) on sampled
-sequences that the oracle computes one by one.  Work lists are checked for exact
-coverage of every (token, query head, key)."""
+1e-4 (float32).  Outputs start as NaN, so a row that no work item wrote fails.  Small
+batches are compared element by element in full; the five full-size workloads (in the
+launch configuration the benchmark times, serial and two-stream) on every row, the
+oracle computing each sequence alone.  Work lists are checked for exact coverage of
+every (token, query head, key)."""
 import sys
 
 import numpy as np
@@ -108,8 +109,10 @@ def check_work_coverage(md, b, wl):
         assert len(got) == ns >= 2
 
 
-def run_full(wl, rope_base=None, check_coverage=True):
-    """Whole batch through GPU and oracle; compares everything element by element."""
+def run_full(wl, rope_base=None, check_coverage=True, concurrent=False):
+    """Whole batch through GPU and oracle; compares everything element by element.
+    Outputs start as NaN, so a row that no work item wrote fails.  With ``concurrent``
+    the two-stream call runs too (into its own output) and is compared the same way."""
     base = wl.rope_base if rope_base is None else rope_base
     eng = _engine(wl)
     qkv_in = W.make_qkv(wl)
@@ -118,8 +121,11 @@ def run_full(wl, rope_base=None, check_coverage=True):
     pool = pool_in.cuda()
     b = eng.finalize(wl.n_new, wl.seen, wl.block_lists)
     eng.append_rotary(qkv, pool, base)
-    out = eng.new_out()
-    eng.attention(qkv, pool, out)
+    outs = {"serial": eng.new_out().fill_(float("nan"))}
+    eng.attention(qkv, pool, outs["serial"])
+    if concurrent:
+        outs["two-stream"] = eng.new_out().fill_(float("nan"))
+        eng.attention_concurrent(qkv, pool, outs["two-stream"])
     torch.cuda.synchronize()
 
     md = eng.metadata()
@@ -142,10 +148,14 @@ def run_full(wl, rope_base=None, check_coverage=True):
         assert np.array_equal(pool_gpu[:, 1], pool_ref[:, 1])  # values: raw, bit exact
         _assert_within_one_ulp(pool_gpu[:, 0], pool_ref[:, 0], wl.dtype, "rotated K / pool")
     ref = O.ragged_attention(q_ref, pool_ref, ref_md, Hq, Hkv, wl.block_size, wl.dtype)
-    got = O.storage_to_f64(_np_storage(out), wl.dtype)
-    err = np.max(np.abs(got - ref))
-    assert err <= TOL[wl.dtype], f"{wl.name}: max abs err {err}"
-    return err
+    worst = 0.0
+    for which, out in outs.items():
+        got = O.storage_to_f64(_np_storage(out), wl.dtype)
+        assert np.isfinite(got).all(), f"{wl.name} ({which}): rows not written"
+        err = float(np.max(np.abs(got - ref)))
+        assert err <= TOL[wl.dtype], f"{wl.name} ({which}): max abs err {err}"
+        worst = max(worst, err)
+    return worst, b, eng.metadata()
 
 
 # ---------------------------------------------------------------- small batches ----
@@ -223,6 +233,45 @@ def test_long_prefill_chunk_many_tiles():
     run_full(wl)
 
 
+SPLIT_CASES = [  # name, dtype, Hq, Hkv, d, bs, (n_new, seen) per sequence
+    # lean one head per wave, two-stage form (G 4, d 128), one long decode beside a chunk
+    ("lean_g4_d128", "bf16", 8, 2, 128, 64, [(1, 20000), (40, 300), (1, 150), (1, 5000)]),
+    # lean two heads per wave (G 8)
+    ("lean2_g8_d128", "bf16", 16, 2, 128, 64, [(1, 30000), (1, 900), (33, 2000)]),
+    # lean one head per wave, one stage (G 1)
+    ("lean_g1_d64", "bf16", 2, 2, 64, 128, [(1, 16000), (25, 100), (1, 63)]),
+    # grouped kernel (G 16)
+    ("grouped_g16_d128", "bf16", 32, 2, 128, 64, [(1, 12000), (1, 1), (17, 4000)]),
+    # per-wave kernel, bf16 over 16-key blocks
+    ("perwave_g2_bf16", "bf16", 4, 2, 128, 16, [(1, 9000), (1, 777), (9, 50)]),
+    # per-wave kernel, float32
+    ("perwave_g2_f32", "f32", 4, 2, 64, 32, [(1, 12000), (1, 3000), (12, 80)]),
+]
+
+
+@pytest.mark.parametrize("case", [c[0] for c in SPLIT_CASES])
+def test_long_decode_many_splits(case):
+    """One long decode in a small batch is cut into dozens of splits (MIN_SPLIT_TILES
+    keeps splits at four tiles), so the combine merges its partials over several of its
+    load batches, each rescaling the sums of the ones before.  The serial and the
+    two-stream call are both compared with the oracle."""
+    name, dt, Hq, Hkv, d, bs, seqs = next(c for c in SPLIT_CASES if c[0] == case)
+    wl = W.random_workload(61, dtype=dt, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                           block_size=bs, n_seqs=len(seqs))
+    wl.n_new = np.array([a for a, _ in seqs], dtype=np.int32)
+    wl.seen = np.array([b for _, b in seqs], dtype=np.int32)
+    need = [W.blocks_needed(a + b, bs) for a, b in seqs]
+    wl.num_blocks = sum(need) + 3
+    perm = np.random.default_rng(62).permutation(wl.num_blocks).astype(np.int32)
+    at = np.cumsum([0] + need)
+    wl.block_lists = [perm[at[i]:at[i + 1]] for i in range(len(seqs))]
+    _say(f"case many splits {name}")
+    err, b, md = run_full(wl, concurrent=True)
+    most = int(md["combine_work"][:, 3].max())
+    assert most >= 32, f"only {most} splits"
+    _say(f"  {name}: {most} splits, max-abs err {err:.3e}")
+
+
 def test_empty_batch_on_gpu():
     wl = W.random_workload(1, dtype="bf16")
     eng = _engine(wl)
@@ -254,44 +303,40 @@ def test_rejects_host_memory_as_device_buffer():
 
 
 # ---------------------------------------------------------- full-size workloads ----
+#
+# Every sequence of every full-size workload is compared with the oracle, in the launch
+# configuration the benchmark times (the serial call and the two-stream call, each into
+# its own NaN-filled output, so a row no work item wrote fails).  The GPU pass runs once
+# per workload (cached across its parts); each part then checks a share of the
+# sequences, so no single test runs long.  The oracle takes each sequence alone on a
+# sub-pool of just its blocks, read from a pool regenerated from the same seed (the
+# pre-append history), so no host copy of a whole pool is ever made.
+
+FULL_PARTS = {"decode_mha32": 1, "splitfuse768_gqa4": 1, "full8192_gqa4": 4,
+              "full8192_prefill_gqa4": 2, "long_decode_gqa8": 4}
+_FULL = {}
 
 
-def _sample_seqs(wl, k_dec=4, k_chunk=2):
-    """Longest and shortest sequences of each kind, plus seeded extras."""
-    rng = np.random.default_rng(123)
-    L = wl.seen + wl.n_new
-    dec = np.nonzero(wl.n_new == 1)[0]
-    chk = np.nonzero(wl.n_new > 1)[0]
-    pick = []
-    for idx, k in ((dec, k_dec), (chk, k_chunk)):
-        if len(idx) == 0:
-            continue
-        order = idx[np.argsort(L[idx])]
-        sel = {int(order[0]), int(order[-1])}
-        extra = rng.permutation(idx)
-        for e in extra:
-            if len(sel) >= k:
-                break
-            sel.add(int(e))
-        pick.extend(sorted(sel))
-    return pick
-
-
-def run_sampled(wl):
-    """Full workload on the GPU (same launches the benchmark times); the oracle runs
-    each sampled sequence alone on a sub-pool holding just that sequence's blocks."""
+def _full_gpu_pass(name):
+    """GPU side of one full-size workload, shared by its parts: finalize, append, the
+    serial and the two-stream attention; whole-batch checks of metadata, work coverage,
+    pool canaries and V placement."""
+    if name in _FULL:
+        return _FULL[name]
+    _FULL.clear()
+    torch.cuda.empty_cache()
+    wl = W.make_workload(name)
+    _say(f"gpu pass {name} S={wl.S} T={wl.T} blocks={wl.num_blocks}")
     eng = _engine(wl)
     qkv_in = W.make_qkv(wl)
     pool = W.make_pool_history(wl, device="cuda")
-    seqs = _sample_seqs(wl)
-    nb = [W.blocks_needed(int(a) + int(b), wl.block_size) for a, b in zip(wl.n_new, wl.seen)]
-    hist = {i: _np_storage(pool[torch.as_tensor(wl.block_lists[i][:nb[i]].astype(np.int64),
-                                                  device="cuda")]) for i in seqs}
     qkv = qkv_in.cuda()
     b = eng.finalize(wl.n_new, wl.seen, wl.block_lists)
     eng.append_rotary(qkv, pool, wl.rope_base)
-    out = eng.new_out()
-    eng.attention(qkv, pool, out)
+    out_s = eng.new_out().fill_(float("nan"))
+    out_c = eng.new_out().fill_(float("nan"))
+    eng.attention(qkv, pool, out_s)
+    eng.attention_concurrent(qkv, pool, out_c)
     torch.cuda.synchronize()
 
     md = eng.metadata()
@@ -300,8 +345,9 @@ def run_sampled(wl):
         assert np.array_equal(md[k], ref_md[k]), k
     check_work_coverage(md, b, wl)
 
-    # canary: pool rows other than this pass's slots are unchanged
+    # the history before this pass's append, regenerated from the same seed
     fresh = W.make_pool_history(wl, device="cuda")
+    # canary: pool rows other than this pass's slots are unchanged
     changed = (fresh != pool).any(dim=4).any(dim=2).any(dim=1)  # [num_blocks, bs]
     written = torch.zeros_like(changed)
     blk = torch.as_tensor(ref_md["block_ids"][ref_md["block_offsets"][ref_md["token_to_seq"]] +
@@ -310,40 +356,65 @@ def run_sampled(wl):
     slot = torch.as_tensor((ref_md["pos"] % wl.block_size).astype(np.int64), device="cuda")
     written[blk, slot] = True
     assert not bool((changed & ~written).any())
+    del changed, written
     # V placement bit exact for every token
     Hq, Hkv = wl.n_q_heads, wl.n_kv_heads
     assert torch.equal(pool[blk, 1, :, slot, :].cpu(), qkv_in[:, Hq + Hkv:])
-    del fresh
+    st = {
+        "wl": wl, "ref_md": ref_md, "fresh": fresh,
+        "qkv_in": _np_storage(qkv_in), "q": _np_storage(qkv),
+        "k_new": _np_storage(pool[blk, 0, :, slot, :]),
+        "out_s": _np_storage(out_s), "out_c": _np_storage(out_c),
+        "checked": set(), "parts": set(),
+    }
+    del pool
+    _FULL[name] = st
+    return st
 
-    qkv_np = _np_storage(qkv_in)
-    out_np = _np_storage(out)
-    q_np = _np_storage(qkv)
-    worst = 0.0
+
+def check_full_part(name, part):
+    """The oracle on this part's sequences (every nparts-th one), each alone on a
+    sub-pool of its own blocks: rotated Q and K within one ulp, attention of the serial
+    and the two-stream call within tolerance, every row of both."""
+    st = _full_gpu_pass(name)
+    wl, ref_md = st["wl"], st["ref_md"]
+    Hq, Hkv, bs = wl.n_q_heads, wl.n_kv_heads, wl.block_size
+    nparts = FULL_PARTS[name]
+    worst = {"serial": 0.0, "two-stream": 0.0}
+    seqs = list(range(part, wl.S, nparts))
     for i in seqs:
         t0, t1 = int(ref_md["cu_seqlens"][i]), int(ref_md["cu_seqlens"][i + 1])
-        sub_ids = np.arange(nb[i], dtype=np.int32)
-        m1 = O.batch_metadata([wl.n_new[i]], [wl.seen[i]], [sub_ids], wl.block_size)
-        q_ref, sub_pool = O.append_rotary(qkv_np[t0:t1], hist[i], m1, Hq, Hkv, wl.block_size,
+        nb = int(ref_md["block_offsets"][i + 1] - ref_md["block_offsets"][i])
+        ids = ref_md["block_ids"][int(ref_md["block_offsets"][i]):][:nb].astype(np.int64)
+        hist = _np_storage(st["fresh"][torch.as_tensor(ids, device="cuda")])
+        m1 = O.batch_metadata([wl.n_new[i]], [wl.seen[i]], [np.arange(nb, dtype=np.int32)], bs)
+        q_ref, sub_pool = O.append_rotary(st["qkv_in"][t0:t1], hist, m1, Hq, Hkv, bs,
                                           wl.rope_base, wl.dtype)
-        _assert_within_one_ulp(q_np[t0:t1, :Hq], q_ref[:, :Hq], wl.dtype, f"Q seq {i}")
+        _assert_within_one_ulp(st["q"][t0:t1, :Hq], q_ref[:, :Hq], wl.dtype, f"Q seq {i}")
         pos = ref_md["pos"][t0:t1]
-        gk = _np_storage(pool[blk[t0:t1], 0, :, slot[t0:t1], :])
-        rk = sub_pool[pos // wl.block_size, 0, :, pos % wl.block_size, :]
-        _assert_within_one_ulp(gk, rk, wl.dtype, f"K seq {i}")
-        ref = O.ragged_attention(q_ref, sub_pool, m1, Hq, Hkv, wl.block_size, wl.dtype)
-        got = O.storage_to_f64(out_np[t0:t1], wl.dtype)
-        err = float(np.max(np.abs(got - ref)))
-        worst = max(worst, err)
-        assert err <= TOL[wl.dtype], f"{wl.name} seq {i}: max abs err {err}"
-    # attention output is finite everywhere
-    assert bool(torch.isfinite(out.float()).all())
-    return worst
+        rk = sub_pool[pos // bs, 0, :, pos % bs, :]
+        _assert_within_one_ulp(st["k_new"][t0:t1], rk, wl.dtype, f"K seq {i}")
+        ref = O.ragged_attention(q_ref, sub_pool, m1, Hq, Hkv, bs, wl.dtype)
+        for which, key in (("serial", "out_s"), ("two-stream", "out_c")):
+            got = O.storage_to_f64(st[key][t0:t1], wl.dtype)
+            assert np.isfinite(got).all(), f"{name} seq {i} ({which}): rows not written"
+            err = float(np.max(np.abs(got - ref)))
+            worst[which] = max(worst[which], err)
+            assert err <= TOL[wl.dtype], f"{name} seq {i} ({which}): max abs err {err}"
+        st["checked"].add(i)
+    st["parts"].add(part)
+    if len(st["parts"]) == nparts:
+        assert st["checked"] == set(range(wl.S))  # every sequence of the batch compared
+    return len(seqs), worst
 
 
-@pytest.mark.parametrize("name", ["decode_mha32", "splitfuse768_gqa4", "full8192_gqa4",
-                                  "full8192_prefill_gqa4", "long_decode_gqa8"])
-def test_full_size_workloads_sampled(name):
-    wl = W.make_workload(name)
-    _say(f"case {name} S={wl.S} T={wl.T} blocks={wl.num_blocks}")
-    err = run_sampled(wl)
-    _say(f"  {name}: worst sampled max-abs err {err:.3e}")
+@pytest.mark.parametrize("name,part", [(n, p) for n, k in FULL_PARTS.items() for p in range(k)])
+@pytest.mark.timeout(300)
+def test_full_size_workloads_every_row(name, part):
+    _say(f"case {name} part {part + 1}/{FULL_PARTS[name]}")
+    n, worst = check_full_part(name, part)
+    _say(f"  {name} part {part + 1}: {n} sequences, worst max-abs err serial "
+         f"{worst['serial']:.3e}, two-stream {worst['two-stream']:.3e}")
+    if len(_FULL[name]["parts"]) == FULL_PARTS[name]:
+        _FULL.clear()
+        torch.cuda.empty_cache()
