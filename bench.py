@@ -165,17 +165,112 @@ def traffic_from_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, ca
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(wl, qkv_cpu, hist_fn, budget_s):
-    """The oracle as it stands, on a bounded sample of the same batch: sequences in a
-    seeded order (chunks and decodes interleaved), each through the oracle's append and
-    attention on a sub-pool holding its own blocks, until the time budget is spent."""
+def host_cpu():
+    """The host's CPU model and core counts (what the CPU baseline ran on)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity}
+
+
+def _mapped(ref):
+    """An array, or (path, offset, shape, dtype) of one held in a shared-memory file."""
+    if isinstance(ref, np.ndarray):
+        return ref
+    path, off, shape, dt = ref
+    return np.memmap(path, dtype=np.dtype(dt), mode="r", offset=off, shape=tuple(shape))
+
+
+def _oracle_sequence(task):
+    """One sequence through the oracle's append and attention on a sub-pool of its own
+    blocks; returns (new tokens, seconds).  The unit of work of both CPU timings."""
     import oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    n, seen, qrows, sub_pool, Hq, Hkv, bs, base, dtype = task
+    qrows, sub_pool = _mapped(qrows), _mapped(sub_pool)
+    t0 = time.perf_counter()
+    m1 = O.batch_metadata([n], [seen], [np.arange(sub_pool.shape[0], dtype=np.int32)], bs)
+    q, p = O.append_rotary(qrows, sub_pool, m1, Hq, Hkv, bs, base, dtype)
+    O.ragged_attention(q, p, m1, Hq, Hkv, bs, dtype)
+    return n, time.perf_counter() - t0
+
+
+_BLAS_LIMIT = None
+
+
+def _single_blas_thread():
+    """Worker initializer: one BLAS thread per process."""
+    global _BLAS_LIMIT
+    from threadpoolctl import threadpool_limits
+    _BLAS_LIMIT = threadpool_limits(1)
+
+
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def mfma_from_counters(csv_path, util_csv, workload, out_path):
+    """Reduce a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE (values summed over every instance: SIMDs, shader
+    engines, XCDs) on the prefill kernel, plus a run of rocprofv3's derived MfmaUtil
+    metric, into per-launch matrix-core figures:
+
+    * mfma_flops_per_launch = 512 x MOPS_BF16 (the counter counts flops / 512);
+    * mfma_busy_frac = MFMA busy cycles / (GUI-active cycles of one XCD x 1024 SIMDs),
+      the derived MfmaUtil's formula (GRBM_GUI_ACTIVE is summed over the 8 XCDs here, so
+      one XCD's count is the sum / 8); MfmaUtil's own value is kept beside it."""
+    sel = lambda n: "prefill_attn_kernel" in n
+    busy = _counter_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", sel)
+    mops = _counter_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", sel)
+    gui = _counter_per_dispatch(csv_path, "GRBM_GUI_ACTIVE", sel)
+    cu = _counter_per_dispatch(csv_path, "SQ_BUSY_CU_CYCLES", sel)
+    util = _counter_per_dispatch(util_csv, "MfmaUtil", sel) if util_csv else {}
+    ids = sorted(busy)
+    fr = [busy[i] / (gui[i] / XCDS * SIMDS) for i in ids]
+    rec = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    rec[f"attn_prefill.hip:{workload}"] = {
+        "source_sha": kernel_source_digest("attn_prefill.hip"),
+        "dispatches": len(ids),
+        "mfma_flops_per_launch": float(np.mean([mops[i] for i in ids])) * 512.0,
+        "mfma_busy_cycles_per_launch": float(np.mean([busy[i] for i in ids])),
+        "gui_active_cycles_per_xcd": float(np.mean([gui[i] for i in ids])) / XCDS,
+        "busy_cu_quad_cycles_per_launch": float(np.mean([cu[i] for i in ids])) if cu else None,
+        "mfma_busy_frac": float(np.mean(fr)),
+        "mfma_busy_frac_per_dispatch": [round(v, 4) for v in fr],
+        "MfmaUtil_percent": float(np.mean(list(util.values()))) if util else None,
+    }
+    json.dump(rec, open(out_path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1))
+
+
+def cpu_baseline(wl, qkv_cpu, hist_fn, budget_s, max_workers=16):
+    """The oracle as it stands, on a bounded sample of the same batch (sequences in a
+    seeded order, chunks and decodes interleaved; each through the oracle's append and
+    attention on a sub-pool holding its own blocks; input staging not timed), two ways:
+
+    * one core: this process with its BLAS held to one thread, sequences one after
+      another until ``budget_s`` of oracle time is spent;
+    * one process per core: ``min(cpu count, affinity, max_workers)`` worker processes
+      (spawned, so none inherits this process's GPU state), each with one BLAS thread,
+      fed sequences in the same order until ``budget_s`` of wall time has passed, then
+      drained; rate = tokens done / wall time from the first submission to the last
+      result (worker start-up and the staging of inputs into a shared-memory file that
+      the workers map excluded).
+
+    ``value`` is the process-per-core rate, ``cores`` its worker count."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+
     rng = np.random.default_rng(2024)
     chunks = [int(i) for i in rng.permutation(np.nonzero(wl.n_new > 1)[0])]
     decs = [int(i) for i in rng.permutation(np.nonzero(wl.n_new == 1)[0])]
@@ -186,31 +281,77 @@ def cpu_baseline(wl, qkv_cpu, hist_fn, budget_s):
         order.extend(decs[:15])
         decs = decs[15:]
     cu = np.concatenate([[0], np.cumsum(wl.n_new)])
-    qkv_np = qkv_cpu
-    done_tok, done_seq, n_chunks, spent = 0, 0, 0, 0.0
-    for i in order:
+
+    def task(i):
         nb = -(-(int(wl.seen[i]) + int(wl.n_new[i])) // wl.block_size)
-        sub_pool = hist_fn(i, nb)  # input staging, not timed
-        t0 = time.perf_counter()
-        m1 = O.batch_metadata([wl.n_new[i]], [wl.seen[i]], [np.arange(nb, dtype=np.int32)],
-                              wl.block_size)
-        q, p = O.append_rotary(qkv_np[cu[i]:cu[i + 1]], sub_pool, m1, wl.n_q_heads,
-                               wl.n_kv_heads, wl.block_size, wl.rope_base, wl.dtype)
-        O.ragged_attention(q, p, m1, wl.n_q_heads, wl.n_kv_heads, wl.block_size, wl.dtype)
-        spent += time.perf_counter() - t0
-        done_tok += int(wl.n_new[i])
-        done_seq += 1
-        n_chunks += int(wl.n_new[i] > 1)
-        if spent >= budget_s:
-            break
+        return (int(wl.n_new[i]), int(wl.seen[i]), qkv_cpu[cu[i]:cu[i + 1]], hist_fn(i, nb),
+                wl.n_q_heads, wl.n_kv_heads, wl.block_size, wl.rope_base, wl.dtype)
+
+    def describe(seqs, tok, secs, what):
+        nch = sum(int(wl.n_new[i] > 1) for i in seqs)
+        return (f"{len(seqs)} of {wl.S} sequences of {wl.name} ({nch} prefill chunks, "
+                f"{len(seqs) - nch} decodes, {tok} of {wl.T} tokens): float64 oracle append + "
+                f"attention, {secs:.1f} s {what}")
+
+    # one core
+    done, tok1, spent = [], 0, 0.0
+    with threadpool_limits(1):
+        for i in order:
+            n, dt = _oracle_sequence(task(i))
+            done.append(i)
+            tok1 += n
+            spent += dt
+            if spent >= budget_s:
+                break
+    single = {"value": tok1 / spent, "unit": "tokens/s", "cores": 1, "blas_threads": 1,
+              "sample": describe(done, tok1, spent, "of oracle time on one core")}
+
+    # one process per core; the inputs go to the workers through one shared-memory file
+    # written before the clock starts (input staging, not timed)
+    import tempfile
+
+    host = host_cpu()
+    workers = max(1, min(host["os_cpu_count"] or 1, host["affinity_cpus"] or 1, max_workers))
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    with tempfile.NamedTemporaryFile(dir=shm, prefix="rbkv_oracle_") as f:
+        refs, off = {}, 0
+        for i in order:
+            t = task(i)
+            pair = []
+            for a in (t[2], t[3]):
+                a = np.ascontiguousarray(a)
+                f.write(a.tobytes())
+                pair.append((f.name, off, a.shape, a.dtype.str))
+                off += a.nbytes
+            refs[i] = t[:2] + tuple(pair) + t[4:]
+        f.flush()
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers, initializer=_single_blas_thread) as pool:
+            pool.map(int, range(workers))  # every worker started before the clock
+            pending, done_m, tokm = [], [], 0
+            t0 = time.perf_counter()
+            for i in order:
+                while len(pending) >= 2 * workers:
+                    j, r = pending.pop(0)
+                    tokm += r.get()[0]
+                    done_m.append(j)
+                pending.append((i, pool.apply_async(_oracle_sequence, (refs[i],))))
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            for j, r in pending:
+                tokm += r.get()[0]
+                done_m.append(j)
+            wall = time.perf_counter() - t0
     return {
-        "value": done_tok / spent,
+        "value": tokm / wall,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"{done_seq} of {wl.S} sequences of {wl.name} ({n_chunks} prefill chunks, "
-                   f"{done_seq - n_chunks} decodes, {done_tok} of {wl.T} tokens): float64 "
-                   f"oracle append + attention, {spent:.1f} s"),
+        "blas_threads_per_process": 1,
+        "sample": describe(done_m, tokm, wall, f"of wall time over {workers} worker processes "
+                                              f"(one BLAS thread each)"),
+        "single_core": single,
+        "host": host,
     }
 
 
@@ -443,6 +584,164 @@ def kv_offload_leg(wl, eng, pool, stream, n=1024, reps=5, warm=2):
     }
 
 
+# Every measured configuration, in the order of the table in workloads: the tiny float32
+# batch, MHA decode, SplitFuse 768, the full-budget batch, its prefill chunks alone and
+# long-context decode.
+CONFIG_WORKLOADS = ("tiny_f32", "decode_mha32", "splitfuse768_gqa4", "full8192_gqa4",
+                    "full8192_prefill_gqa4", "long_decode_gqa8")
+
+
+def measured_mfma(label, workload):
+    """Matrix-core counters per launch from committed rocprofv3 runs (profiles/mfma.json),
+    if they were taken on the current source of that kernel (else None)."""
+    p = os.path.join(ROOT, "profiles", "mfma.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{label}:{workload}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_digest(KERNEL_GROUPS[label][0]):
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "MfmaUtil_percent", "mfma_flops_per_launch",
+                                "dispatches") if k in rec}
+
+
+def time_steps(wl, eng, qkv, pool, out, stream, steps, warmup, two_stream=True):
+    """Serial steps (metadata rebuild, append, prefill, decode, combine) with HIP events
+    between the phases on the stream they run on, then (``two_stream``) steps with the
+    attention as the two-stream call and events around it.  Both bracketed by
+    synchronisations; wall-clock seconds of each loop and the per-step event times."""
+    import torch
+
+    from ragged_blocked_kv_amd import PHASE_COMBINE, PHASE_DECODE, PHASE_PREFILL
+
+    def step(ev=None):
+        def mark(k):
+            if ev is not None:
+                ev[k].record(stream)
+        mark(0)
+        eng.rebuild(stream=stream)
+        mark(1)
+        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
+        mark(2)
+        eng.attention_phase(PHASE_PREFILL, qkv, pool, out, stream=stream)
+        mark(3)
+        eng.attention_phase(PHASE_DECODE, qkv, pool, out, stream=stream)
+        mark(4)
+        eng.attention_phase(PHASE_COMBINE, qkv, pool, out, stream=stream)
+        mark(5)
+
+    for _ in range(warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall_serial = time.perf_counter() - t0
+
+    # The same work with the prefill and the decodes sharing the chip
+    # (ragged_blocked_attention_concurrent, bit-identical output).
+    def step_concurrent(ev=None):
+        eng.rebuild(stream=stream)
+        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        eng.attention_concurrent(qkv, pool, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)  # after the join: both streams' work is done
+
+    wall, ts = None, None
+    if two_stream:
+        for _ in range(warmup):
+            step_concurrent()
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step_concurrent(cev[k])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ts = np.array([cev[k][0].elapsed_time(cev[k][1]) for k in range(steps)])
+    return {
+        "phase_ms": {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
+                                       for k in range(steps)]))
+                     for j, p in enumerate(PHASES)},
+        "step_ms": np.array([events[k][0].elapsed_time(events[k][5]) for k in range(steps)]),
+        "attn_ms": np.array([events[k][2].elapsed_time(events[k][5]) for k in range(steps)]),
+        "two_stream_ms": ts, "wall_serial": wall_serial, "wall_two_stream": wall,
+    }
+
+
+def figures(wl, tm):
+    """The per-configuration figures: attention tokens/s and whole-attention HBM
+    fraction (serial phases and the two-stream call), each dominant kernel against its
+    own peak, append and combine."""
+    work = algorithmic_work(wl)
+    ph = tm["phase_ms"]
+    pct = lambda a: [round(float(np.percentile(a, q)) * 1e3, 1) for q in (10, 50, 90)]
+
+    def attention(ms, samples):
+        gbs = work["attention_bytes"] / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 1), "us_p10_p50_p90": pct(samples),
+                "tokens_per_s": wl.T / (ms * 1e-3), "attention_algorithmic_GBs": gbs,
+                "hbm_frac_attention": gbs / HBM_PEAK_GBS}
+
+    serial_ms = ph["prefill"] + ph["decode"] + ph["combine"]
+    att = {"bytes": work["attention_bytes"], "serial": attention(serial_ms, tm["attn_ms"]),
+           "two_stream": None}
+    if tm["two_stream_ms"] is not None:
+        att["two_stream"] = attention(float(np.median(tm["two_stream_ms"])), tm["two_stream_ms"])
+    att["timed_call"] = "two-stream" if att["two_stream"] else "serial"
+    att["hbm_frac"] = (att["two_stream"] or att["serial"])["hbm_frac_attention"]
+    dec = pre = None
+    # float32 batches run every item (chunks too) on the vector-ALU decode kernel
+    dec_bytes = work["decode_bytes"] if wl.dtype == "bf16" else work["attention_bytes"]
+    if dec_bytes > 0 and ph["decode"] > 0:
+        gbs = dec_bytes / (ph["decode"] * 1e-3) / 1e9
+        dec = {"kernel": decode_kernel_name(wl), "us": round(ph["decode"] * 1e3, 2),
+               "bytes": dec_bytes, "GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    if wl.dtype == "bf16" and work["prefill_flops"] > 0 and ph["prefill"] > 0:
+        tfs = work["prefill_flops"] / (ph["prefill"] * 1e-3) / 1e12
+        pre = {"kernel": "prefill_attn_kernel", "us": round(ph["prefill"] * 1e3, 2),
+               "flops": work["prefill_flops"], "TFLOPs": tfs,
+               "mfma_frac": tfs / MFMA_BF16_PEAK_TFS}
+    app_gbs = work["append_bytes"] / (ph["append"] * 1e-3) / 1e9
+    return {
+        "S": wl.S, "T": wl.T, "dtype": wl.dtype,
+        "attention": att,
+        "decode": dec,
+        "prefill": pre,
+        "append": {"us": round(ph["append"] * 1e3, 2), "bytes": work["append_bytes"],
+                   "hbm_frac": app_gbs / HBM_PEAK_GBS},
+        "combine_us": round(ph["combine"] * 1e3, 2),
+        "rebuild_us": round(ph["rebuild"] * 1e3, 2),
+        "step_us_p10_p50_p90": pct(tm["step_ms"]),
+    }
+
+
+def measure_config(name, dev, stream, steps, warmup):
+    """One configuration end to end on its own buffers (its pool freed afterwards)."""
+    import torch
+
+    import workloads as W
+    from ragged_blocked_kv_amd.runtime import Engine
+
+    wl = W.make_workload(name)
+    eng = Engine.for_workload(wl, device=dev)
+    qkv = W.make_qkv(wl).to(dev)
+    pool = W.make_pool_history(wl, device=dev)
+    out = torch.empty((wl.T, wl.n_q_heads, wl.head_dim), dtype=qkv.dtype, device=dev)
+    eng.finalize(wl.n_new, wl.seen, wl.block_lists, stream=stream)
+    fig = figures(wl, time_steps(wl, eng, qkv, pool, out, stream, steps, warmup))
+    del pool, qkv, out, eng
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return fig
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -457,6 +756,8 @@ def main():
     ap.add_argument("--no-serving", action="store_true", help="skip the SplitFuse serving leg")
     ap.add_argument("--no-gathers", action="store_true", help="skip the row-gather leg")
     ap.add_argument("--no-offload", action="store_true", help="skip the KV offload leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration measurements (every other workload)")
     ap.add_argument("--serial-only", action="store_true",
                     help="time only the serial step (value from it): every library kernel then "
                          "runs once per step with its whole work list, as the kernel-trace and "
@@ -467,7 +768,14 @@ def main():
                     metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV",
                              "CAL_BYTES"),
                     help="reduce rocprofv3 counter CSVs into profiles/traffic.json and exit")
+    ap.add_argument("--mfma-from", nargs=2, default=None, metavar=("PMC_CSV", "MFMAUTIL_CSV"),
+                    help="reduce rocprofv3 matrix-core counter CSVs into profiles/mfma.json and "
+                         "exit")
     args = ap.parse_args()
+    if args.mfma_from:
+        mfma_from_counters(args.mfma_from[0], args.mfma_from[1], args.workload,
+                           os.path.join(ROOT, "profiles", "mfma.json"))
+        return
     if args.traffic_from:
         f, w, cf, cw, cb = args.traffic_from
         traffic_from_counters(f, w, cf, cw, int(cb), args.workload,
@@ -485,7 +793,6 @@ def main():
     import torch
 
     import workloads as W
-    from ragged_blocked_kv_amd import PHASE_COMBINE, PHASE_DECODE, PHASE_PREFILL
     from ragged_blocked_kv_amd.runtime import Engine
 
     dev = torch.device("cuda:0")
@@ -529,59 +836,8 @@ def main():
             hist[i] = blk.view(torch.int16).numpy().view(np.uint16) if wl.dtype == "bf16" \
                 else blk.numpy()
 
-    def step(ev=None):
-        def mark(k):
-            if ev is not None:
-                ev[k].record(stream)
-        mark(0)
-        eng.rebuild(stream=stream)
-        mark(1)
-        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
-        mark(2)
-        eng.attention_phase(PHASE_PREFILL, qkv, pool, out, stream=stream)
-        mark(3)
-        eng.attention_phase(PHASE_DECODE, qkv, pool, out, stream=stream)
-        mark(4)
-        eng.attention_phase(PHASE_COMBINE, qkv, pool, out, stream=stream)
-        mark(5)
-
-    # Serial step with HIP events between the phases: the per-kernel times the roofline
-    # and the phase breakdown use.
-    for _ in range(args.warmup):
-        step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall_serial = time.perf_counter() - t0
-
-    # The timed step: the same work with the prefill and the decodes sharing the chip
-    # (ragged_blocked_attention_concurrent, bit-identical output), bracketed by
-    # synchronisations.
-    def step_concurrent(ev=None):
-        eng.rebuild(stream=stream)
-        eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        eng.attention_concurrent(qkv, pool, out, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)  # after the join: both streams' work is done
-
-    wall = wall_serial
-    two_stream = None
-    if not args.serial_only:
-        for _ in range(args.warmup):
-            step_concurrent()
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(args.steps):
-            step_concurrent(cev[k])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        two_stream = np.array([cev[k][0].elapsed_time(cev[k][1]) for k in range(args.steps)])
+    tm = time_steps(wl, eng, qkv, pool, out, stream, args.steps, args.warmup,
+                    two_stream=not args.serial_only)
 
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
@@ -589,26 +845,37 @@ def main():
     offload = None if args.no_offload else kv_offload_leg(wl, eng, pool, stream)
     serving = None if args.no_serving else serving_leg(wl, eng, qkv, pool, out, stream)
 
-    phase_ms = {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
-                                  for k in range(args.steps)]))
-                for j, p in enumerate(PHASES)}
-    step_ev = np.array([events[k][0].elapsed_time(events[k][5]) for k in range(args.steps)])
-    attn_ev = np.array([events[k][2].elapsed_time(events[k][5]) for k in range(args.steps)])
+    fig = figures(wl, tm)
+    phase_ms = tm["phase_ms"]
+    wall = tm["wall_two_stream"] if tm["wall_two_stream"] is not None else tm["wall_serial"]
     ms_per_step = wall * 1e3 / args.steps
-    work = algorithmic_work(wl)
-    dec_gbs = work["decode_bytes"] / (phase_ms["decode"] * 1e-3) / 1e9 if phase_ms["decode"] else 0
-    pre_tfs = work["prefill_flops"] / (phase_ms["prefill"] * 1e-3) / 1e12 \
-        if phase_ms["prefill"] else 0
-    if phase_ms["prefill"] >= phase_ms["decode"]:
-        roof = {"kernel": "prefill_attn_kernel", "bound": "mfma", "achieved": pre_tfs,
-                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": pre_tfs / MFMA_BF16_PEAK_TFS,
+    if fig["prefill"] and (not fig["decode"] or phase_ms["prefill"] >= phase_ms["decode"]):
+        pf = fig["prefill"]
+        roof = {"kernel": "prefill_attn_kernel", "bound": "mfma", "achieved": pf["TFLOPs"],
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": pf["mfma_frac"],
                 "traffic": measured_traffic("attn_prefill.hip", wl.name),
-                "per_launch": {"flops": work["prefill_flops"], "us": phase_ms["prefill"] * 1e3}}
+                "per_launch": {"flops": pf["flops"], "us": pf["us"]}}
     else:
-        roof = {"kernel": decode_kernel_name(wl), "bound": "hbm", "achieved": dec_gbs,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+        dc = fig["decode"]
+        roof = {"kernel": dc["kernel"], "bound": "hbm", "achieved": dc["GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dc["hbm_frac"],
                 "traffic": measured_traffic("attn_decode.hip", wl.name),
-                "per_launch": {"bytes": work["decode_bytes"], "us": phase_ms["decode"] * 1e3}}
+                "per_launch": {"bytes": dc["bytes"], "us": dc["us"]}}
+    # The step-level figure next to the dominant kernel's: the whole attention (every K/V
+    # row and Q/output of the batch once) over the timed call's time.
+    roof["attention_call"] = fig["attention"]["timed_call"]
+    roof["attention_frac_hbm"] = fig["attention"]["hbm_frac"]
+    roof["prefill_mfma_counters"] = measured_mfma("attn_prefill.hip", wl.name)
+
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for name in CONFIG_WORKLOADS:
+            if name == wl.name:
+                configs[name] = fig
+                continue
+            configs[name] = measure_config(name, dev, stream, min(args.steps, 20), 3)
+            print(f"bench: measured {name}", file=sys.stderr, flush=True)
 
     base = None
     if not args.no_cpu_baseline:
@@ -616,7 +883,6 @@ def main():
                             if wl.dtype == "bf16" else qkv_cpu.numpy(),
                             lambda i, nb: hist[i], args.cpu_seconds)
 
-    attn_ms = phase_ms["prefill"] + phase_ms["decode"] + phase_ms["combine"]
     rec = {
         "metric": "ragged attention tokens/s on 1 GPU + % peak HBM GB/s (decode) / % MFMA (prefill)",
         "value": wl.T * args.steps / wall,
@@ -646,31 +912,15 @@ def main():
         "roofline": roof,
         "cpu_baseline": base,
         "phases_us": {p: round(v * 1e3, 2) for p, v in phase_ms.items()},
-        "attention_only": {
-            "tokens_per_s": wl.T / (attn_ms * 1e-3),
-            "hbm_frac_decode": dec_gbs / HBM_PEAK_GBS,
-            "mfma_frac_prefill": pre_tfs / MFMA_BF16_PEAK_TFS,
-            "attention_algorithmic_GBs": work["attention_bytes"] / (attn_ms * 1e-3) / 1e9,
-            # every K/V row and Q/output of the batch once, over the whole attention time
-            "hbm_frac_attention": work["attention_bytes"] / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "us_p10_p50_p90": [round(float(np.percentile(attn_ev, q)) * 1e3, 1)
-                               for q in (10, 50, 90)],
-        },
-        "step_us_p10_p50_p90": [round(float(np.percentile(step_ev, q)) * 1e3, 1)
-                                for q in (10, 50, 90)],
+        "attention_only": fig["attention"]["serial"],
+        "step_us_p10_p50_p90": fig["step_us_p10_p50_p90"],
         "finalize_call_us": finalize_us,
-        "attention_two_stream": None if two_stream is None else {
-            "us_p10_p50_p90": [round(float(np.percentile(two_stream, q)) * 1e3, 1)
-                               for q in (10, 50, 90)],
-            "tokens_per_s": wl.T / (float(np.median(two_stream)) * 1e-3),
-            # every K/V row and Q/output of the batch once, over the two-stream attention time
-            "hbm_frac_attention": work["attention_bytes"] / (float(np.median(two_stream)) * 1e-3)
-                                  / 1e9 / HBM_PEAK_GBS,
-        },
-        "serial_step": {"ms_per_step": wall_serial * 1e3 / args.steps,
-                        "tokens_per_s": wl.T * args.steps / wall_serial,
+        "attention_two_stream": fig["attention"]["two_stream"],
+        "serial_step": {"ms_per_step": tm["wall_serial"] * 1e3 / args.steps,
+                        "tokens_per_s": wl.T * args.steps / tm["wall_serial"],
                         "step": "the same phases one after another on one stream, with HIP "
                                 "events between them (the per-kernel times above)"},
+        "configs": configs,
         "ledger": ledger,
         "splitfuse_serving": serving,
         "gathers": gathers,
