@@ -34,7 +34,9 @@
  *   containers, and a metaclass that checks your weights".)
  * - The caller owns all memory.  The library allocates no device memory, keeps no
  *   mutable global state and never synchronises the stream; every call only enqueues
- *   work on the given stream.
+ *   work on the given stream.  (One exception, for callers that cannot allocate:
+ *   ragged_blocked_attention_noalloc uses a static scratch array the library holds per
+ *   GPU.)
  * - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Device
  *   buffers must belong to the current HIP device.
  * - Element types: RBKV_DTYPE_F32 (float) or RBKV_DTYPE_BF16 (bfloat16 bit patterns).
@@ -217,6 +219,32 @@ rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* 
 rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
                                      const void* qkv, const void* kv_pool, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the library's static scratch: the largest split-K workspace (as
+ * rbkv_workspace_bytes reports it) that ragged_blocked_attention_noalloc accepts.
+ * 64 MiB covers every measured batch (the 256-sequence long-context decode batch needs
+ * about 32 MiB). */
+#define RBKV_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* ragged_blocked_attention without a caller workspace and without any allocation: for
+ * callers that cannot allocate device memory or pass one (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The split-K partials go to a
+ * fixed array of RBKV_STATIC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU it runs on, until the process ends (its address is looked up once per device,
+ * at the first call on that device).  Same kernels, same result (bit for bit) as
+ * ragged_blocked_attention.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine) and never synchronises.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, or two host threads) race and may corrupt each other's results, so order
+ * them (one stream).  Nothing in the array needs to start at zero; it keeps the last
+ * call's partials.
+ * Errors: WORKSPACE (the batch needs more split-K scratch than
+ * RBKV_STATIC_SCRATCH_BYTES: use ragged_blocked_attention with a workspace), and as
+ * ragged_blocked_attention (INVALID_ARG, DEVICE_PTR, HIP).  All checks run before
+ * anything is launched. */
+rbkv_status ragged_blocked_attention_noalloc(const rbkv_shape* shape, const rbkv_batch* batch,
+                                             const void* qkv, const void* kv_pool, void* out,
+                                             void* stream);
 
 /* One phase of ragged_blocked_attention (RBKV_PHASE_*), for callers that place other
  * work between the phases or time them separately.  Running PREFILL, DECODE, COMBINE in

@@ -18,7 +18,8 @@ import numpy as np
 __all__ = [
     "RbkvError", "Shape", "Batch", "lib", "status_string", "check",
     "rbkv_metadata_bytes", "rbkv_workspace_bytes", "ragged_batch_finalize",
-    "blocked_kv_append_rotary", "ragged_blocked_attention", "ragged_batch_rebuild",
+    "blocked_kv_append_rotary", "ragged_blocked_attention", "ragged_blocked_attention_noalloc",
+    "STATIC_SCRATCH_BYTES", "ragged_batch_rebuild",
     "ragged_blocked_attention_phase", "ragged_blocked_attention_concurrent",
     "ragged_embedding_gather", "ragged_logits_gather",
     "rbkv_kv_host_bytes", "blocked_kv_offload", "blocked_kv_restore", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
@@ -31,6 +32,7 @@ OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_BLOCKS, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 ERR_WORKSPACE, ERR_DEVICE_PTR, ERR_HIP, ERR_HOST_MEMORY = 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16 = 0, 1
 PHASE_ALL, PHASE_PREFILL, PHASE_DECODE, PHASE_COMBINE = 0, 1, 2, 3
+STATIC_SCRATCH_BYTES = 64 << 20  # RBKV_STATIC_SCRATCH_BYTES
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librbkv.so")
 
@@ -42,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "ragged_batch_rebuild",
     "blocked_kv_append_rotary",
     "ragged_blocked_attention",
+    "ragged_blocked_attention_noalloc",
     "ragged_blocked_attention_phase",
     "ragged_blocked_attention_concurrent",
     "ragged_embedding_gather",
@@ -163,6 +166,10 @@ def lib():
         L.ragged_blocked_attention.argtypes = [
             ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.ragged_blocked_attention_noalloc.restype = ctypes.c_int32
+        L.ragged_blocked_attention_noalloc.argtypes = [
+            ctypes.POINTER(Shape), ctypes.POINTER(Batch), ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -258,6 +265,13 @@ def ragged_blocked_attention(shape: Shape, batch: Batch, qkv, kv_pool, out, work
     return lib().ragged_blocked_attention(ctypes.byref(shape), ctypes.byref(batch), _ptr(qkv),
                                           _ptr(kv_pool), _ptr(out), _ptr(workspace),
                                           int(workspace_bytes), _stream(stream))
+
+
+def ragged_blocked_attention_noalloc(shape: Shape, batch: Batch, qkv, kv_pool, out,
+                                     stream=None) -> int:
+    return lib().ragged_blocked_attention_noalloc(ctypes.byref(shape), ctypes.byref(batch),
+                                                  _ptr(qkv), _ptr(kv_pool), _ptr(out),
+                                                  _stream(stream))
 
 
 def ragged_batch_rebuild(shape: Shape, batch: Batch, stream=None) -> int:

@@ -28,6 +28,7 @@ SOURCES = [
     "attn_decode.hip",
     "attn_prefill.hip",
     "attn_combine.hip",
+    "static_scratch.hip",
     "gather.hip",
     "kv_offload.hip",
 ]

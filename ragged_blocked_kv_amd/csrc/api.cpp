@@ -341,10 +341,13 @@ namespace {
 
 // Argument checks of an attention call (phases pre / dec / comb requested and non-empty).
 // *launch is false when there is nothing to launch (then no buffer is inspected).
+// Checks shared by the attention calls.  workspace_owned: the workspace is the library's
+// static scratch (its size is checked by the caller, and it is not a caller allocation
+// that the pointer queries could describe), so only the caller's buffers are queried.
 rbkv_status check_attention(const rbkv_shape* shape, const rbkv_batch* batch, bool pre,
                             bool dec, bool comb, const void* qkv, const void* kv_pool,
                             const void* out, const void* workspace, size_t workspace_bytes,
-                            bool* launch) {
+                            bool* launch, bool workspace_owned = false) {
   *launch = false;
   rbkv_status st = check_shape(shape);
   if (st != RBKV_OK) return st;
@@ -363,8 +366,24 @@ rbkv_status check_attention(const rbkv_shape* shape, const rbkv_batch* batch, bo
   if ((st = check_device(qkv, qkv_bytes)) != RBKV_OK) return st;
   if ((st = check_device(kv_pool, pool_bytes)) != RBKV_OK) return st;
   if ((st = check_device(out, out_bytes)) != RBKV_OK) return st;
-  if (need > 0 && (st = check_device(workspace, need)) != RBKV_OK) return st;
+  if (need > 0 && !workspace_owned && (st = check_device(workspace, need)) != RBKV_OK)
+    return st;
   *launch = true;
+  return RBKV_OK;
+}
+
+// The launches of one attention call on one stream (checks already done).
+rbkv_status launch_attention(const rbkv_shape& s, const rbkv_batch& b, bool pre, bool dec,
+                             bool comb, const void* qkv, const void* kv_pool, void* out,
+                             void* workspace, hipStream_t hs) {
+  hipError_t err = hipSuccess;
+  if (pre) err = launch_prefill(s, b, qkv, kv_pool, out, hs);
+  if (err == hipSuccess && dec) err = launch_decode(s, b, qkv, kv_pool, out, (float*)workspace, hs);
+  if (err == hipSuccess && comb) err = launch_combine(s, b, (const float*)workspace, out, hs);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return RBKV_ERR_HIP;
+  }
   return RBKV_OK;
 }
 
@@ -385,19 +404,36 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
   rbkv_status st = check_attention(shape, batch, pre, dec, comb, qkv, kv_pool, out, workspace,
                                    workspace_bytes, &launch);
   if (st != RBKV_OK || !launch) return st;
-  const rbkv_shape& s = *shape;
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t err = hipSuccess;
-  if (pre) err = launch_prefill(s, *batch, qkv, kv_pool, out, hs);
-  if (err == hipSuccess && dec)
-    err = launch_decode(s, *batch, qkv, kv_pool, out, (float*)workspace, hs);
-  if (err == hipSuccess && comb)
-    err = launch_combine(s, *batch, (const float*)workspace, out, hs);
-  if (err != hipSuccess) {
+  return launch_attention(*shape, *batch, pre, dec, comb, qkv, kv_pool, out, workspace,
+                          (hipStream_t)stream);
+}
+
+rbkv_status ragged_blocked_attention_noalloc(const rbkv_shape* shape, const rbkv_batch* batch,
+                                             const void* qkv, const void* kv_pool, void* out,
+                                             void* stream) {
+  rbkv_status st = check_shape(shape);
+  if (st != RBKV_OK) return st;
+  if (!batch) return RBKV_ERR_INVALID_ARG;
+  if (!same_shape(batch->shape, *shape)) return RBKV_ERR_INVALID_ARG;
+  size_t need = 0;
+  if ((st = rbkv_workspace_bytes(shape, batch, &need)) != RBKV_OK) return st;
+  if (need > (size_t)RBKV_STATIC_SCRATCH_BYTES) return RBKV_ERR_WORKSPACE;
+  const bool pre = batch->n_prefill_items > 0;
+  const bool dec = batch->n_decode_items > 0;
+  const bool comb = batch->n_combine_items > 0;
+  // A non-null stand-in lets the shared checks run; the real address is resolved only
+  // when there is something to launch.
+  bool launch = false;
+  st = check_attention(shape, batch, pre, dec, comb, qkv, kv_pool, out,
+                       need > 0 ? (const void*)1 : nullptr, need, &launch, true);
+  if (st != RBKV_OK || !launch) return st;
+  void* ws = nullptr;
+  if (need > 0 && static_scratch(&ws) != hipSuccess) {
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
   }
-  return RBKV_OK;
+  return launch_attention(*shape, *batch, pre, dec, comb, qkv, kv_pool, out, ws,
+                          (hipStream_t)stream);
 }
 
 namespace {

@@ -167,6 +167,10 @@ hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* 
 hipError_t launch_combine(const rbkv_shape& s, const rbkv_batch& b, const float* ws,
                           void* out, hipStream_t stream);
 
+// Address of the library's static scratch array (RBKV_STATIC_SCRATCH_BYTES) on the current
+// device, resolved once per device (static_scratch.hip).
+hipError_t static_scratch(void** ptr);
+
 // Row gather: mode 0 takes source row idx[r] (zero row outside [0, n_src)), mode 1 takes
 // idx[r + 1] - 1.  row_bytes is a multiple of 16; rows * row_bytes / 16 < 2^31.
 hipError_t launch_gather_rows(int mode, const void* src, void* dst, const int32_t* idx,

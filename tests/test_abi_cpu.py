@@ -154,6 +154,30 @@ def test_append_and_attention_validation():
     assert R.blocked_kv_append_rotary(s, b, FAKE, FAKE, 1e4) == R.ERR_INVALID_ARG
 
 
+def test_noalloc_attention_validation():
+    """The allocation-free call checks its arguments like the others and refuses a batch
+    whose split-K partials exceed the static scratch, before any HIP call."""
+    s = shape()
+    b = R.Batch()
+    b.shape = s
+    b.T = 3
+    b.n_partials = 5
+    assert R.ragged_blocked_attention_noalloc(s, b, FAKE, None, FAKE) == R.ERR_INVALID_ARG
+    assert R.ragged_blocked_attention_noalloc(shape(head_dim=128), b, FAKE, FAKE, FAKE) == \
+        R.ERR_INVALID_ARG
+    assert R.ragged_blocked_attention_noalloc(shape(head_dim=96), b, FAKE, FAKE, FAKE) == \
+        R.ERR_UNSUPPORTED
+    # partials of G * (d + 2) floats: just fitting, then one slot too many
+    per = 2 * (64 + 2) * 4
+    fit = R.STATIC_SCRATCH_BYTES // per
+    b.n_partials = fit + 1
+    assert R.rbkv_workspace_bytes(s, b)[1] > R.STATIC_SCRATCH_BYTES
+    assert R.ragged_blocked_attention_noalloc(s, b, FAKE, FAKE, FAKE) == R.ERR_WORKSPACE
+    b.T = 0  # an empty batch launches nothing, whatever its counts
+    b.n_partials = fit
+    assert R.ragged_blocked_attention_noalloc(s, b, FAKE, FAKE, FAKE) == R.OK
+
+
 def test_workspace_holds_claim_counter_for_overlapped_decodes():
     """bf16 batches with both phases, groups of <= 8 heads and 64-key blocks get a
     256-byte-aligned item counter after the partials (the two-stream call's persistent
