@@ -225,9 +225,10 @@ def mfma_from_counters(csv_path, util_csv, workload, out_path):
     metric, into per-launch matrix-core figures:
 
     * mfma_flops_per_launch = 512 x MOPS_BF16 (the counter counts flops / 512);
-    * mfma_busy_frac = MFMA busy cycles / (GUI-active cycles of one XCD x 1024 SIMDs),
-      the derived MfmaUtil's formula (GRBM_GUI_ACTIVE is summed over the 8 XCDs here, so
-      one XCD's count is the sum / 8); MfmaUtil's own value is kept beside it."""
+    * MfmaUtil_percent: rocprofv3's derived metric, MFMA busy cycles summed over the SIMDs /
+      (the largest XCD's GUI-active cycles x 1024 SIMDs), from its own run;
+    * mfma_busy_frac: the same ratio over the mean XCD's GUI-active cycles (GRBM_GUI_ACTIVE
+      is summed over the 8 XCDs in this run, so the mean is the sum / 8)."""
     sel = lambda n: "prefill_attn_kernel" in n
     busy = _counter_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", sel)
     mops = _counter_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", sel)
@@ -603,7 +604,7 @@ def measured_mfma(label, workload):
         return None
     if not rec or rec.get("source_sha") != kernel_source_digest(KERNEL_GROUPS[label][0]):
         return None
-    return {k: rec[k] for k in ("mfma_busy_frac", "MfmaUtil_percent", "mfma_flops_per_launch",
+    return {k: rec[k] for k in ("MfmaUtil_percent", "mfma_busy_frac", "mfma_flops_per_launch",
                                 "dispatches") if k in rec}
 
 
