@@ -33,6 +33,7 @@ def _run(wl, concurrent, reps=3):
 
 
 @pytest.mark.parametrize("name", ["random_bf16", "random_f32", "lean_g4_d128", "lean_g1_d64",
+                                  "reg_g1_d128",
                                   "lean_g2_unsplit", "lean_g8_d128", "lean_g6_d64",
                                   "splitfuse768_gqa4", "full8192_gqa4"])
 def test_concurrent_equals_serial(name):
@@ -46,6 +47,9 @@ def test_concurrent_equals_serial(name):
     elif name == "lean_g4_d128":
         wl = W.random_workload(33, dtype="bf16", n_q_heads=16, n_kv_heads=4, head_dim=128,
                                block_size=64, n_seqs=40, max_new=300, max_seen=3000)
+    elif name == "reg_g1_d128":
+        wl = W.random_workload(38, dtype="bf16", n_q_heads=8, n_kv_heads=8, head_dim=128,
+                               block_size=64, n_seqs=30, max_new=200, max_seen=2500)
     elif name == "lean_g1_d64":
         wl = W.random_workload(34, dtype="bf16", n_q_heads=6, n_kv_heads=6, head_dim=64,
                                block_size=128, n_seqs=30, max_new=200, max_seen=2000)

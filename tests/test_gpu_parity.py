@@ -238,8 +238,10 @@ SPLIT_CASES = [  # name, dtype, Hq, Hkv, d, bs, (n_new, seen) per sequence
     ("lean_g4_d128", "bf16", 8, 2, 128, 64, [(1, 20000), (40, 300), (1, 150), (1, 5000)]),
     # lean two heads per wave (G 8)
     ("lean2_g8_d128", "bf16", 16, 2, 128, 64, [(1, 30000), (1, 900), (33, 2000)]),
-    # lean one head per wave, one stage (G 1)
+    # lean one head per wave, one stage (G 1, d 64)
     ("lean_g1_d64", "bf16", 2, 2, 64, 128, [(1, 16000), (25, 100), (1, 63)]),
+    # register-only kernel (G 1, d 128), with short items a wave sees no key of
+    ("reg_g1_d128", "bf16", 4, 4, 128, 64, [(1, 14000), (30, 200), (1, 20), (1, 70)]),
     # grouped kernel (G 16)
     ("grouped_g16_d128", "bf16", 32, 2, 128, 64, [(1, 12000), (1, 1), (17, 4000)]),
     # per-wave kernel, bf16 over 16-key blocks
