@@ -153,10 +153,12 @@ rbkv_status rbkv_metadata_bytes(const rbkv_shape* shape, size_t* dev_bytes,
 
 /* Device workspace ragged_blocked_attention needs for `batch` (split-K partial
  * results; the scratch output the blocked attention kernel is handed in the same
- * section), plus, for a bf16 batch with both prefill chunks and decodes, groups of at
- * most four heads and blocks of 64+ keys, a 256-byte-aligned item counter that
- * ragged_blocked_attention_concurrent uses.  0 when no decode is split and no counter is
- * needed.  Pure host computation. */
+ * section), plus a 256-byte-aligned item counter for decodes that run as persistent
+ * workgroups: bf16 batches over blocks of 64+ keys, groups of at most eight heads, with
+ * both prefill chunks and decodes (ragged_blocked_attention_concurrent), and, at head
+ * dim 128 with groups of 2-4 heads, any batch with decodes (the serial call as well).
+ * The calls reset the counter themselves (a kernel, no memset).  0 when no decode is
+ * split and no counter is needed.  Pure host computation. */
 rbkv_status rbkv_workspace_bytes(const rbkv_shape* shape, const rbkv_batch* batch,
                                  size_t* bytes);
 

@@ -87,11 +87,33 @@ rbkv_status launch_build(const rbkv_shape& s, char* dm, int32_t S, hipStream_t s
   return RBKV_OK;
 }
 
-// Workspace: the split-K partials, then (when the two-stream call runs the decodes as
-// persistent workgroups) the 256-byte-aligned counter they claim items from.
+// Decodes of bf16 groups of 2-4 heads at head dim 128 over blocks of 64+ keys run as
+// persistent workgroups in the serial call too: two per CU of the two-stage lean form,
+// taking items from a counter, instead of one workgroup per item (full-budget decode
+// 635 -> 608 us, SplitFuse 330 -> 319 us; single-head groups and groups of 5-8 measured
+// equal or slower persistent, and keep one workgroup per item).
+constexpr int SERIAL_PERSISTENT_WG_PER_CU = 2;
+bool serial_persistent(const rbkv_shape& s) {
+  const int32_t G = s.n_q_heads / s.n_kv_heads;
+  return decode_lean_ok(s) && s.head_dim == 128 && G >= 2 && G <= 4;
+}
+
+// Workspace: the split-K partials, then (when decodes run as persistent workgroups: in
+// the two-stream call, and in the serial call for the shapes above) the 256-byte-aligned
+// counter they claim items from.
 constexpr size_t CLAIM_BYTES = 256;
 bool uses_claim(const rbkv_shape& s, const rbkv_batch& b) {
-  return decode_lean_ok(s) && b.n_decode_items > 0 && b.n_prefill_items > 0;
+  return decode_lean_ok(s) && b.n_decode_items > 0 &&
+         (b.n_prefill_items > 0 || serial_persistent(s));
+}
+
+// Compute units of the current device.
+hipError_t cu_count(int* n_cu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && *n_cu < 1) e = hipErrorInvalidDevice;
+  return e;
 }
 size_t claim_offset(const rbkv_shape& s, const rbkv_batch& b) {
   const int32_t G = s.n_q_heads / s.n_kv_heads;
@@ -378,7 +400,19 @@ rbkv_status launch_attention(const rbkv_shape& s, const rbkv_batch& b, bool pre,
                              void* workspace, hipStream_t hs) {
   hipError_t err = hipSuccess;
   if (pre) err = launch_prefill(s, b, qkv, kv_pool, out, hs);
-  if (err == hipSuccess && dec) err = launch_decode(s, b, qkv, kv_pool, out, (float*)workspace, hs);
+  if (err == hipSuccess && dec) {
+    if (serial_persistent(s)) {
+      int n_cu = 0;
+      int32_t* claim = (int32_t*)((char*)workspace + claim_offset(s, b));
+      err = cu_count(&n_cu);
+      if (err == hipSuccess) err = launch_decode_claim_reset(claim, hs);
+      if (err == hipSuccess)
+        err = launch_decode_persistent(s, b, qkv, kv_pool, out, (float*)workspace, claim,
+                                       SERIAL_PERSISTENT_WG_PER_CU * n_cu, hs, 2);
+    } else {
+      err = launch_decode(s, b, qkv, kv_pool, out, (float*)workspace, hs);
+    }
+  }
   if (err == hipSuccess && comb) err = launch_combine(s, b, (const float*)workspace, out, hs);
   if (err != hipSuccess) {
     (void)hipGetLastError();
@@ -609,10 +643,8 @@ constexpr int OVERLAP_MAIN_WG_PER_CU_2ST = 2;
 rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                  const void* kv_pool, void* out, char* ws, hipStream_t hs,
                                  hipStream_t hside, hipEvent_t fork, hipEvent_t join) {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      n_cu < 1) {
+  int n_cu = 0;
+  if (cu_count(&n_cu) != hipSuccess) {
     (void)hipGetLastError();
     return RBKV_ERR_HIP;
   }

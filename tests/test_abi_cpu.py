@@ -181,7 +181,9 @@ def test_noalloc_attention_validation():
 def test_workspace_holds_claim_counter_for_overlapped_decodes():
     """bf16 batches with both phases, groups of <= 8 heads and 64-key blocks get a
     256-byte-aligned item counter after the partials (the two-stream call's persistent
-    decodes claim items from it); other shapes and one-phase batches do not."""
+    decodes claim items from it), and so do decode batches at head dim 128 with groups
+    of 2-4 heads (the serial call's decodes are persistent there); other shapes and
+    batches do not."""
     def need(s, n_partials, n_dec, n_pre):
         b = R.Batch()
         b.shape = s
@@ -196,6 +198,13 @@ def test_workspace_holds_claim_counter_for_overlapped_decodes():
     assert need(lean, 0, 7, 2) == 256                # unsplit decodes: the counter alone
     assert need(lean, 5, 7, 0) == part               # no prefill: no overlap, no counter
     assert need(lean, 5, 0, 2) == part
+    # head dim 128, groups of 2-4: the serial call's decodes are persistent too
+    lean128 = shape(block_size=64, head_dim=128)
+    part128 = 5 * 2 * (128 + 2) * 4                  # 5200 bytes of partials
+    assert need(lean128, 5, 7, 0) == 5376 + 256      # decode-only batch: counter as well
+    assert need(lean128, 5, 0, 2) == part128         # no decode: no counter
+    assert need(shape(block_size=64, head_dim=128, n_q_heads=2, n_kv_heads=2), 5, 7, 0) == \
+        5 * 1 * (128 + 2) * 4                        # single-head groups: one workgroup per item
     assert need(shape(block_size=32), 5, 7, 2) == part          # blocks under 64 keys
     assert need(shape(block_size=64, dtype="f32"), 5, 7, 2) == part
     g8 = shape(block_size=64, n_q_heads=16, n_kv_heads=2)        # groups of 8 heads: counter
