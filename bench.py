@@ -90,7 +90,7 @@ KERNEL_GROUPS = {
     "attn_prefill.hip": ("attn_prefill.hip", ("prefill_attn_kernel",)),
     "attn_decode.hip": ("attn_decode.hip", ("decode_attn_kernel", "decode_group_kernel",
                                             "decode_lean_kernel", "decode_lean2_kernel",
-                                            "decode_reg_kernel")),
+                                            "decode_reg_kernel", "decode_mfma_kernel")),
     "append_rotary.hip": ("append_rotary.hip", ("append_rotary_kernel",)),
     "attn_combine.hip": ("attn_combine.hip", ("combine_kernel",)),
     "meta_build.hip": ("meta_build.hip", ("meta_build_kernel",)),
@@ -101,14 +101,15 @@ KERNEL_GROUPS = {
 
 
 def decode_kernel_name(wl):
-    """The decode kernel a workload runs: bf16 over 64-key blocks runs a lean workgroup
-    with one K/V tile (one wave per head for groups of up to 4 heads, two heads per wave
-    for 5-8), except single-head groups at head dim 128, which run the register-only
-    kernel; other bf16 groups of 5+ heads the two-stage grouped kernel; float32, and bf16
-    groups of up to 4 over smaller blocks, one wave per item."""
+    """The decode kernel a workload runs: bf16 over 64-key blocks at head dim 128 runs the
+    matrix-core kernel for groups of 2-16 heads and the register-only kernel for single
+    heads; at head dim 64 a lean workgroup with one K/V tile (one wave per head for groups
+    of up to 4 heads, two heads per wave for 5-8); other bf16 groups of 5+ heads the
+    two-stage grouped kernel; float32, and bf16 groups of up to 4 over smaller blocks, one
+    wave per item."""
     g = wl.n_q_heads // wl.n_kv_heads
-    if wl.dtype == "bf16" and g == 1 and wl.block_size >= 64 and wl.head_dim == 128:
-        return "decode_reg_kernel"
+    if wl.dtype == "bf16" and wl.block_size >= 64 and wl.head_dim == 128:
+        return "decode_reg_kernel" if g == 1 else "decode_mfma_kernel"
     if wl.dtype == "bf16" and g <= 8 and wl.block_size >= 64:
         return "decode_lean_kernel" if g <= 4 else "decode_lean2_kernel"
     if wl.dtype == "bf16" and g > 4:

@@ -87,23 +87,21 @@ rbkv_status launch_build(const rbkv_shape& s, char* dm, int32_t S, hipStream_t s
   return RBKV_OK;
 }
 
-// Decodes of bf16 groups of 2-4 heads at head dim 128 over blocks of 64+ keys run as
-// persistent workgroups in the serial call too: two per CU of the two-stage lean form,
-// taking items from a counter, instead of one workgroup per item (full-budget decode
-// 635 -> 608 us, SplitFuse 330 -> 319 us; single-head groups and groups of 5-8 measured
-// equal or slower persistent, and keep one workgroup per item).
-constexpr int SERIAL_PERSISTENT_WG_PER_CU = 2;
-bool serial_persistent(const rbkv_shape& s) {
-  const int32_t G = s.n_q_heads / s.n_kv_heads;
-  return decode_lean_ok(s) && s.head_dim == 128 && G >= 2 && G <= 4;
-}
+// Decodes on the matrix-core kernel run as persistent workgroups in the serial call too:
+// one per CU with three tile stages per wave (97 KB of LDS), taking items from a counter,
+// instead of one workgroup per item (long decode 2262 -> 2177 us; with two stages and two
+// workgroups per CU 2190 us, full-budget 614 against 605 us).  Single-head groups keep
+// one workgroup per item on the register-only kernel.
+constexpr int SERIAL_PERSISTENT_WG_PER_CU = 1;
+constexpr int SERIAL_PERSISTENT_STAGES = 3;
+bool serial_persistent(const rbkv_shape& s) { return decode_mfma_ok(s); }
 
 // Workspace: the split-K partials, then (when decodes run as persistent workgroups: in
 // the two-stream call, and in the serial call for the shapes above) the 256-byte-aligned
 // counter they claim items from.
 constexpr size_t CLAIM_BYTES = 256;
 bool uses_claim(const rbkv_shape& s, const rbkv_batch& b) {
-  return decode_lean_ok(s) && b.n_decode_items > 0 &&
+  return decode_persistent_ok(s) && b.n_decode_items > 0 &&
          (b.n_prefill_items > 0 || serial_persistent(s));
 }
 
@@ -128,9 +126,10 @@ bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
 // Split size for single-token decodes: about the kernel's target number of items overall.
 int32_t choose_split_tiles(const rbkv_shape& s, int64_t decode_tiles_total) {
   const int64_t target =
-      decode_lean_ok(s) ? (s.n_q_heads / s.n_kv_heads <= 4 ? DECODE_TARGET_ITEMS_LEAN
-                                                          : DECODE_TARGET_ITEMS_LEAN2)
-                        : decode_grouped(s) ? DECODE_TARGET_ITEMS_GROUPED : DECODE_TARGET_ITEMS;
+      decode_persistent_ok(s) ? (s.n_q_heads / s.n_kv_heads <= 4 ? DECODE_TARGET_ITEMS_LEAN
+                                                                : DECODE_TARGET_ITEMS_LEAN2)
+      : decode_grouped(s)     ? DECODE_TARGET_ITEMS_GROUPED
+                              : DECODE_TARGET_ITEMS;
   int64_t st = cdiv64(decode_tiles_total, target);
   if (st < MIN_SPLIT_TILES) st = MIN_SPLIT_TILES;
   if (st > MAX_SPLIT_TILES) st = MAX_SPLIT_TILES;
@@ -408,7 +407,8 @@ rbkv_status launch_attention(const rbkv_shape& s, const rbkv_batch& b, bool pre,
       if (err == hipSuccess) err = launch_decode_claim_reset(claim, hs);
       if (err == hipSuccess)
         err = launch_decode_persistent(s, b, qkv, kv_pool, out, (float*)workspace, claim,
-                                       SERIAL_PERSISTENT_WG_PER_CU * n_cu, hs, 2);
+                                       SERIAL_PERSISTENT_WG_PER_CU * n_cu, hs,
+                                       SERIAL_PERSISTENT_STAGES);
     } else {
       err = launch_decode(s, b, qkv, kv_pool, out, (float*)workspace, hs);
     }
@@ -628,15 +628,15 @@ rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* 
 
 namespace {
 
-// The two-stream call for lean-decode shapes: persistent decode workgroups, two per CU,
-// start beside the prefill on the side stream and share the chip with it; once the
-// prefill is done a second launch on the main stream joins them: four one-stage
-// workgroups per CU, or, for head dim 128 and groups of 2-4 heads, two of the two-stage
-// form (no prefill workgroup is left to share a CU with; SplitFuse batch 381 -> 377 us,
-// full-budget batch equal within 1%).  Both take items from one counter, so they finish
-// together whatever the split of the work.  (Sizes measured on the full-budget and
-// SplitFuse batches: one per CU beside the prefill, or more than three, was slower; the
-// second launch's size matters within 1-2%.)
+// The two-stream call for shapes with a persistent decode: decode workgroups, two per CU,
+// start beside the prefill on the side stream and take the CUs it leaves; once the
+// prefill is done a second launch on the main stream joins them: two per CU of the
+// matrix-core kernel (two tile stages per wave; full-budget batch 1085 -> 1059 us and
+// SplitFuse 367 -> 359 us against the lean kernels), or four one-stage lean workgroups
+// per CU at head dim 64.  Both take items from one counter, so they finish together
+// whatever the split of the work.  (Sizes measured with the lean kernels on the
+// full-budget and SplitFuse batches: one per CU beside the prefill, or more than three,
+// was slower; the second launch's size matters within 1-2%.)
 constexpr int OVERLAP_SIDE_WG_PER_CU = 2;
 constexpr int OVERLAP_MAIN_WG_PER_CU = 4;
 constexpr int OVERLAP_MAIN_WG_PER_CU_2ST = 2;
@@ -650,8 +650,9 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
   }
   int32_t* claim = (int32_t*)(ws + claim_offset(s, b));
   float* partials = (float*)ws;
-  const bool two_stage = s.head_dim == 128 && s.n_q_heads / s.n_kv_heads >= 2 &&
-                         s.n_q_heads / s.n_kv_heads <= 4;
+  // The matrix-core decode runs two tile stages per wave (66 KB, two workgroups per CU)
+  // on both streams; the head-dim-64 lean decode one stage (four per CU on the main stream).
+  const bool two_stage = decode_mfma_ok(s);
   // The counter reset runs on the side stream ahead of the side decodes, so the prefill
   // starts on the main stream at once; the join event is recorded right after the reset
   // and the main stream waits for that record before its own decode launch (long done by

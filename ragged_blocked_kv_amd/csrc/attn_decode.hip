@@ -24,6 +24,9 @@ namespace {
 
 // K/V tile rows are read once per work item: non-temporal loads (measured 4-7% faster
 // decode than plain loads on the MHA, SplitFuse and full-budget batches).
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4v lds_s16x4v;
+
 __device__ __forceinline__ u32x4 ldnt(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
@@ -525,26 +528,20 @@ void decode_group_kernel(
 }
 
 // Lean grouped decode for bf16 caches over blocks of at least 64 keys, groups of up to
-// four heads: NW = 4 wavefronts of at most 96 registers, one per query head of the kv
-// group (waves past G repeat the last head and write nothing), and one 64-key K/V tile in LDS (32 KB at head
-// dim 128) with nothing else there: the softmax weights reach the P.V lanes through
-// ds_bpermute, which needs no LDS allocation, and the query row sits in scalar registers.
-// The tile is loaded straight from HBM into LDS by all the waves from a uniform block base.
-// ST = 1: each lane copies its V chunks to registers before the barrier that frees the
-// tile, so the next tile's loads fly while P.V is summed, and the other workgroups on the
-// CU (five four-wave ones fit) hide the rest of the latency.  ST = 2: two tile stages, one
-// barrier per tile, after which the next tile goes into the other stage at once, so every
-// workgroup always has a tile in flight; two workgroups share a CU at head dim 128 (random
-// 16 KiB tiles stream fastest with about two in flight per CU: five one-stage workgroups
-// per CU read 8% slower in a load-only probe).  Arithmetic and order are those of the
-// kernels above (same results, bit for bit).  Work items, split-K partition and partial
-// layout are those of the kernels above; with a claim counter the workgroups are
-// persistent and take items from it.  (A four-wave workgroup would also fit in what a
-// prefill workgroup leaves free on its CU, two waves of 208 registers per SIMD and 128 KB
-// of LDS; measured, sharing CUs that way was slower than letting the two kernels divide
-// the CUs between them.)
-template <int D, int NW, int ST>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ST == 1 ? 5 : 2, ST == 1 ? 5 : 2)))
+// four heads (used at head dim 64; head dim 128 runs on the matrix-core kernel below):
+// NW = 4 wavefronts of at most 96 registers, one per query head of the kv group (waves
+// past G repeat the last head and write nothing), and one 64-key K/V tile in LDS with
+// nothing else there: the softmax weights reach the P.V lanes through ds_bpermute, which
+// needs no LDS allocation, and the query row sits in scalar registers.  The tile is
+// loaded straight from HBM into LDS by all the waves from a uniform block base.  Each lane
+// copies its V chunks to registers before the barrier that frees the tile, so the next
+// tile's loads fly while P.V is summed, and the other workgroups on the CU (five fit)
+// hide the rest of the latency.  Arithmetic and order are those of the kernels above
+// (same results, bit for bit).  Work items, split-K partition and partial layout are
+// those of the kernels above; with a claim counter the workgroups are persistent and take
+// items from it.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(5, 5)))
 void decode_lean_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
@@ -560,10 +557,8 @@ void decode_lean_kernel(
   constexpr int NI = CPR;                    // P.V: row groups per tile
   // The loader takes one K swizzle per thread: each load must cover a multiple of 16 rows.
   static_assert(TILE_CHUNKS % NT == 0 && (NT / CPR) % 16 == 0, "loader geometry");
-  static_assert(ST == 1 || ST == 2, "stages");
-  constexpr uint32_t TILE_BYTES = 64 * D * 2;
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[ST * 64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[ST * 64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[64 * D];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // With a claim counter the workgroup is persistent: it takes item after item from the
@@ -615,7 +610,7 @@ void decode_lean_kernel(
     const uint32_t ld_kc = (uint32_t)(ld_c ^ kswz(ld_r0)) * 16u, ld_vc = (uint32_t)ld_c * 16u;
     // Blocks hold at least 64 keys, so a tile lies in one block: a uniform base and 32-bit
     // lane offsets.  Rows past the end of the split load its last key (never read unmasked).
-    auto issue_tile = [&](int32_t t, const int32_t* ids, uint32_t stage_off) {
+    auto issue_tile = [&](int32_t t, const int32_t* ids) {
       const int32_t key0 = t * 64;
       const uint16_t* base = pool_g + (size_t)ids[0] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
       const int32_t rmax = key_end - 1 - key0;
@@ -623,8 +618,8 @@ void decode_lean_kernel(
       for (int i = 0; i < NLD; ++i) {
         const uint32_t roff = (uint32_t)min(ld_r0 + i * (NT / CPR), rmax) * (D * 2);
         const uint32_t off = i * NT * 16;
-        load_lds16_nt_s(base, roff + ld_kc, k_dst0 + stage_off + off);
-        load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + stage_off + off);
+        load_lds16_nt_s(base, roff + ld_kc, k_dst0 + off);
+        load_lds16_nt_s(base + v_off, roff + ld_vc, v_dst0 + off);
       }
     };
 
@@ -636,7 +631,7 @@ void decode_lean_kernel(
     }
     int32_t ids[1];
     fetch_ids(t_begin, ids);
-    issue_tile(t_begin, ids, 0);
+    issue_tile(t_begin, ids);
     fetch_ids(min(t_begin + 1, t_end - 1), ids);
 
     float m_run = -INFINITY, lsum = 0.f, o[8];
@@ -655,17 +650,10 @@ void decode_lean_kernel(
 
     for (int32_t tt = t_begin; tt < t_end; ++tt) {
       wait_vmcnt<0>();  // this wave's share of tile tt
-      __syncthreads();  // every wave's share (two stages: and every wave is done with tile tt-1)
-      const uint32_t soff = ((tt - t_begin) & (ST - 1)) * TILE_BYTES;  // this tile's stage
-      if constexpr (ST == 2) {
-        if (tt + 1 < t_end) {
-          issue_tile(tt + 1, ids, soff ^ TILE_BYTES);
-          fetch_ids(min(tt + 2, t_end - 1), ids);
-        }
-      }
+      __syncthreads();  // every wave's share
       const int32_t key0 = tt * 64;
       asm volatile("" : "+v"(krow), "+v"(vcol), "+v"(pidx));
-      const uint32_t kr = krow + soff, vc = vcol + soff;
+      const uint32_t kr = krow, vc = vcol;
 
       // Scores: lane = key.
       float s = 0.f;
@@ -687,12 +675,10 @@ void decode_lean_kernel(
   #pragma unroll
       for (int i = 0; i < NI; ++i)
         vr[i] = *(const u32x4*)((const char*)Vt + vc + i * (KPI * CPR * 16));
-      if constexpr (ST == 1) {
-        if (tt + 1 < t_end) {
-          __syncthreads();  // every wave is done with the tile before it is overwritten
-          issue_tile(tt + 1, ids, 0);
-          fetch_ids(min(tt + 2, t_end - 1), ids);
-        }
+      if (tt + 1 < t_end) {
+        __syncthreads();  // every wave is done with the tile before it is overwritten
+        issue_tile(tt + 1, ids);
+        fetch_ids(min(tt + 2, t_end - 1), ids);
       }
       __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
@@ -1169,6 +1155,234 @@ void decode_reg_kernel(
   }  // items
 }
 
+// Decode on the matrix cores for bf16 caches at head dim 128 over blocks of at least 64
+// keys, for groups of up to 16 query heads.  The four wavefronts of a workgroup each take
+// 16 keys of every 64-key tile of the item and run their own pipeline with no workgroup
+// barrier: the wave's K and V rows go from HBM straight into its own LDS slices
+// (global_load_lds_dwordx4, ST stages, the next tile in flight while this one is computed).
+// Per tile and wave:
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over four 32-dim steps: rows are the wave's 16
+//                   keys, columns the group's query heads (columns past G repeat the last
+//                   head), K fragments from LDS, Q^T in registers for the whole item;
+//   online softmax  lane (g, j) holds the scores of keys 4g..4g+3 for head j, so the
+//                   running maximum of head j is lane-local once the four lane groups
+//                   agree; it moves only past a slack of 2^8 (a cross-lane max when a lane
+//                   asks for it), and the weights are rounded to bf16 as they are summed;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16 per 16-dim block: the weights are already in
+//                   the operand layout (the S^T accumulator layout), V^T fragments come from
+//                   transposing LDS reads (ds_read_b64_tr_b16).
+// K slices carry the XOR swizzle chunk ^ key % 16 (fragment reads hit 16 distinct bank
+// groups), V slices chunk ^ 2 (key % 8) (each half-wave of a transposing read covers 64
+// banks).  At the end of the item each wave leaves its unnormalised output in its own LDS
+// region and the four are merged like split-K partials.
+template <int ST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_mfma_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
+    uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
+    const int32_t* __restrict__ tok2seq, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2,
+    int32_t* __restrict__ claim, int32_t n_items) {
+  constexpr int D = 128, NW = 4, NT = NW * 64;
+  constexpr int TE = 16 * D;       // elements of a wave's K (or V) slice of one tile
+  constexpr int RS = D + 4;        // row stride (floats) of a wave's output in the merge
+  constexpr float SLACK = 8.f;
+  static_assert(ST >= 2 && ST <= 3, "stages");
+  static_assert(16 * RS * 4 <= ST * 2 * TE * 2, "merge rows fit the wave's region");
+  __shared__ __attribute__((aligned(16))) uint16_t buf[NW][ST][2 * TE];
+  __shared__ float ml[NW][16][2];
+  __shared__ int32_t claimed;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;
+
+  auto next_item = [&]() -> int32_t {
+    __syncthreads();  // the previous item's merge is read by every wave
+    if (tid == 0) claimed = atomicAdd(claim, 1);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(claimed);
+  };
+
+  // Loader: instruction n of a slice writes LDS bytes 1024n + 16 lane, i.e. key 4n + g,
+  // chunk slot j; the source chunk is chosen so the slot carries the swizzle.
+  uint32_t ld_k[4], ld_v[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int key = 4 * n + g;
+    ld_k[n] = (uint32_t)((j ^ (key & 15)) * 16);
+    ld_v[n] = (uint32_t)((j ^ (2 * (key & 7))) * 16);
+  }
+  // K fragment of step s for key j: chunk 4s + g.  V^T fragment of dim block d: source
+  // lane (g, a, r) (a = lane / 4 % 4, r = lane % 4) reads key 4g + a, dims 16d + 4r .. +3.
+  uint32_t kfo[4], vfo[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kfo[s] = (uint32_t)(j * D + (((4 * s + g) ^ j) * 8));
+  {
+    const int a = (lane >> 2) & 3, r = lane & 3, key = 4 * g + a;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      vfo[d] = (uint32_t)(TE + key * D + ((2 * d + (r >> 1)) ^ (2 * (key & 7))) * 8 + (r & 1) * 4);
+  }
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(&buf[wave][0][0]));
+
+  for (int32_t item = claim ? next_item() : (int32_t)blockIdx.x; item < n_items;
+       item = claim ? next_item() : n_items) {
+    const int4 w = work[item];
+    const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
+    const int32_t seq = tok2seq[token];
+    const int32_t nkeys = pos[token] + 1;
+    const int32_t tiles_total = (nkeys + 63) >> 6;
+    const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
+    const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
+    const int32_t key_end = min(nkeys, t_end * 64);
+    const int32_t* bids = block_ids + block_off[seq];
+    const int bsh = 31 - __builtin_clz(bs);
+    const size_t head_stride = (size_t)bs * D;
+    const size_t blk_stride = (size_t)2 * Hkv * head_stride;
+    const uint32_t v_bytes = (uint32_t)(Hkv * head_stride * 2);
+    const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
+
+    // The wave's 16 keys of tile t into stage st.  A tile lies in one block (blocks hold
+    // at least 64 keys); rows past the end of the split load its last key, whose weight is 0.
+    auto issue = [&](int32_t t, int st) {
+      const int32_t key0 = t * 64;
+      const uint16_t* base = pool_g + (size_t)bids[key0 >> bsh] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
+      const int32_t rmax = key_end - 1 - key0;
+      const uint32_t dst = lds_wave + (uint32_t)st * (2 * TE * 2);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const uint32_t roff = (uint32_t)min(16 * wave + 4 * n + g, rmax) * (D * 2);
+        load_lds16_nt_s(base, roff + ld_k[n], dst + n * 1024);
+        load_lds16_nt_s(base, v_bytes + roff + ld_v[n], dst + TE * 2 + n * 1024);
+      }
+    };
+
+    u32x4 qb[4];
+    float m = -1e30f, l = 0.f;  // finite start: a wave may see no valid key of a short item
+    f32x4 o[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int32_t t, int st) {
+      const uint16_t* kt = &buf[wave][st][0];
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 kf = *(const u32x4*)(kt + kfo[s]);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kf),
+                                                       __builtin_bit_cast(bf16x8v, qb[s]), sacc, 0, 0, 0);
+      }
+      const int32_t k0 = t * 64 + 16 * wave + 4 * g;
+      float sc[4], mt = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = k0 + i < key_end ? sacc[i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, sc[i]);
+      }
+      if (__any(mt > m + SLACK)) {
+        float M = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        const float mnew = M > m + SLACK ? M : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[d] *= alpha;
+        m = mnew;
+      }
+      const uint32_t p01 = pack_bf16x2(__builtin_amdgcn_exp2f(sc[0] - m), __builtin_amdgcn_exp2f(sc[1] - m));
+      const uint32_t p23 = pack_bf16x2(__builtin_amdgcn_exp2f(sc[2] - m), __builtin_amdgcn_exp2f(sc[3] - m));
+      l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p01), as_bf16x2(0x3f803f80u), l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p23), as_bf16x2(0x3f803f80u), l, false);
+      const s16x4v pb = __builtin_bit_cast(s16x4v, u32x2{p01, p23});
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const s16x4v vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(kt + vfo[d]));
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pb, o[d], 0, 0, 0);
+      }
+    };
+
+    // The wave's own pipeline: the item's first ST tiles go out at once, then each tile's
+    // stage is refilled with the tile ST further as soon as it has been computed; before a
+    // tile is read only the loads of later tiles (8 per tile) may be outstanding.
+#pragma unroll
+    for (int u = 0; u < ST; ++u)
+      if (t_begin + u < t_end) issue(t_begin + u, u);
+    // Q^T operand of step s: head j (clamped to the group), dims 32s + 8g .. +8.  The
+    // empty asm makes the compiler complete these loads here (together with the first
+    // tiles, which are needed first anyway), so that no wait it tracks for them falls
+    // inside the tile loop, where it would also drain the next tiles' loads.
+    {
+      const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + min(j, G - 1)) * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qb[s] = ld16(qrow + (4 * s + g) * 8);
+      asm volatile("" : : "v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
+    }
+    int st = 0;
+    for (int32_t t = t_begin; t < t_end; ++t) {
+      const int32_t later = min(t_end - 1 - t, ST - 1);
+      if (ST == 3 && later >= 2) wait_vmcnt<16>();
+      else if (later >= 1) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+      compute(t, st);
+      if (t + ST < t_end) issue(t + ST, st);
+      st = st + 1 == ST ? 0 : st + 1;
+    }
+
+    // Merge: each wave's weight sum over its lane groups, then the four waves through LDS.
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    float* ro = (float*)&buf[wave][0][0];  // this wave's region: its reads of it are done
+    if (j < G) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) *(f32x4*)(ro + j * RS + 16 * d + 4 * g) = o[d];
+      if (g == 0) {
+        ml[wave][j][0] = m;
+        ml[wave][j][1] = l;
+      }
+    }
+    __syncthreads();
+    for (int u = tid; u < G * D; u += NT) {
+      const int h = u / D, dim = u % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, ml[wv][h][0]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) {
+        const float a = __builtin_amdgcn_exp2f(ml[wv][h][0] - M);
+        num = fmaf(a, ((const float*)&buf[wv][0][0])[h * RS + dim], num);
+        den = fmaf(a, ml[wv][h][1], den);
+      }
+      if (slot < 0) {
+        out[((size_t)token * Hq + (size_t)kvh * G + h) * D + dim] = (uint16_t)bf16_rne_f32(num / den);
+      } else {
+        float* part = ws + (size_t)slot * G * (D + 2);
+        if (dim == 0) {
+          part[h] = M;
+          part[G + h] = den;
+        }
+        part[2 * G + (size_t)h * D + dim] = num;
+      }
+    }
+    if (!claim) break;
+  }  // items
+}
+
+template <int ST>
+hipError_t launch_mfma(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                       const void* pool, void* out, float* ws, hipStream_t stream,
+                       int32_t* claim = nullptr, int32_t workgroups = 0) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf(128.f);
+  const int G = s.n_q_heads / s.n_kv_heads;
+  const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
+  hipLaunchKernelGGL((decode_mfma_kernel<ST>), dim3(grid), dim3(256), 0, stream,
+                     (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
+                     (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
+                     b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
+                     scale_log2, claim, b.n_decode_items);
+  return hipGetLastError();
+}
+
 template <int GP>
 hipError_t launch_reg(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                       const void* pool, void* out, float* ws, hipStream_t stream,
@@ -1202,18 +1416,11 @@ hipError_t launch_lean2(const rbkv_shape& s, const rbkv_batch& b, const void* qk
 template <int D, int NW>
 hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                        const void* pool, void* out, float* ws, hipStream_t stream,
-                       int32_t* claim = nullptr, int32_t workgroups = 0, int stages = 0) {
+                       int32_t* claim = nullptr, int32_t workgroups = 0) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int G = s.n_q_heads / s.n_kv_heads;
   const int32_t grid = claim ? std::min(workgroups, b.n_decode_items) : b.n_decode_items;
-  // stages == 0 (the serial call): one workgroup per item, with two tile stages (64 KB,
-  // two workgroups per CU, so a tile load is always in flight) at head dim 128 and groups
-  // of 2-4 heads.  Single-head groups, whose items are whole sequences of mixed length,
-  // keep five one-stage workgroups per CU (with two per CU their tail varied run to run),
-  // and so does head dim 64.  Persistent launches pass their own choice.
-  if (stages == 0) stages = (!claim && D == 128 && G >= 2) ? 2 : 1;
-  auto kern = stages == 2 ? decode_lean_kernel<D, NW, 2> : decode_lean_kernel<D, NW, 1>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((decode_lean_kernel<D, NW>), dim3(grid), dim3(NW * 64), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
                      (const int4*)b.decode_work, b.token_to_seq, b.pos, b.block_offsets,
                      b.block_ids, s.n_q_heads, s.n_kv_heads, G, s.block_size, b.split_tiles,
@@ -1270,12 +1477,16 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
                     void* out, float* ws, hipStream_t stream) {
   const int G = s.n_q_heads / s.n_kv_heads;
   if constexpr (sizeof(T) == 2) {
-    // bf16 groups of up to 8 heads over blocks of 64+ keys: one K/V tile per workgroup,
-    // one wave per head up to 4 heads, two heads per wave for 5-8.
-    if (decode_lean_ok(s)) {
-      if (D == 128 && G == 1) return launch_reg<1>(s, b, qkv, pool, out, ws, stream);
-      return G <= 4 ? launch_lean<D, 4>(s, b, qkv, pool, out, ws, stream)
-                    : launch_lean2<D, 4>(s, b, qkv, pool, out, ws, stream);
+    // Blocks of 64+ keys.  Head dim 128: groups of 2-16 heads on the matrix cores,
+    // single-head groups on the register-only kernel.  Head dim 64, groups of up to 8
+    // heads: one K/V tile per workgroup, one wave per head up to 4 heads, two for 5-8.
+    if constexpr (D == 128) {
+      if (decode_mfma_ok(s)) return launch_mfma<2>(s, b, qkv, pool, out, ws, stream);
+      if (decode_lean_ok(s)) return launch_reg<1>(s, b, qkv, pool, out, ws, stream);
+    } else {
+      if (decode_lean_ok(s))
+        return G <= 4 ? launch_lean<D, 4>(s, b, qkv, pool, out, ws, stream)
+                      : launch_lean2<D, 4>(s, b, qkv, pool, out, ws, stream);
     }
     // Other bf16 groups of 5 or more heads: one wave per head over two LDS tile stages.
     if (decode_grouped(s))
@@ -1299,14 +1510,13 @@ hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream) {
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
                                     int32_t workgroups, hipStream_t stream, int stages) {
-  const bool g4 = s.n_q_heads / s.n_kv_heads <= 4;
-  if (s.head_dim == 128 && s.n_q_heads == s.n_kv_heads)
-    return launch_reg<1>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
-  if (s.head_dim == 128)
-    return g4 ? launch_lean<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups, stages)
-              : launch_lean2<128, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
-  return g4 ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups, stages)
-            : launch_lean2<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+  if (decode_mfma_ok(s))
+    return stages >= 3 ? launch_mfma<3>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+                       : launch_mfma<2>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+  if (s.head_dim == 128) return launch_reg<1>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+  return s.n_q_heads / s.n_kv_heads <= 4
+             ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
+             : launch_lean2<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
 }
 
 hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,

@@ -20,9 +20,10 @@ constexpr int MAX_TOKENS_LIMIT = 1 << 20;
 constexpr int MAX_BLOCKS_LIMIT = 1 << 26;
 // Decode split-K sizing: aim for about this many decode work items per batch (one
 // wavefront each), or DECODE_TARGET_ITEMS_GROUPED for the one-wave-per-head kernel
-// (a workgroup each, two resident per CU; finer items trim its tail).  The lean kernels
-// take fewer, longer items (fewer item starts; the list ends on its shortest items):
-// DECODE_TARGET_ITEMS_LEAN for groups of up to four heads, _LEAN2 for five to eight.
+// (a workgroup each, two resident per CU; finer items trim its tail).  The lean and
+// matrix-core kernels take fewer, longer items (fewer item starts; the list ends on its
+// shortest items): DECODE_TARGET_ITEMS_LEAN for groups of up to four heads, _LEAN2 for
+// larger groups.
 constexpr int64_t DECODE_TARGET_ITEMS = 6144;
 constexpr int64_t DECODE_TARGET_ITEMS_GROUPED = 12288;
 constexpr int64_t DECODE_TARGET_ITEMS_LEAN = 3072;
@@ -48,6 +49,20 @@ inline bool decode_grouped(const rbkv_shape& s) {
 // more keys run on the lean kernel (one wave per head, one K/V tile per workgroup).
 inline bool decode_lean_ok(const rbkv_shape& s) {
   return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads <= 8 && s.block_size >= 64;
+}
+
+// Single-token decodes of bf16 groups of 2-16 query heads at head dim 128 over blocks of
+// 64 or more keys run on the matrix-core kernel (each wave a 16-key slice of every tile).
+inline bool decode_mfma_ok(const rbkv_shape& s) {
+  const int32_t G = s.n_q_heads / s.n_kv_heads;
+  return s.dtype == RBKV_DTYPE_BF16 && s.head_dim == 128 && s.block_size >= 64 && G >= 2 &&
+         G <= MAX_GROUP;
+}
+
+// Shapes whose decodes can run as persistent workgroups draining the decode list through
+// a device counter (launch_decode_persistent).
+inline bool decode_persistent_ok(const rbkv_shape& s) {
+  return decode_lean_ok(s) || decode_mfma_ok(s);
 }
 
 // Tokens of one sequence per prefill workgroup: as many as fit PF_ROWS rows of G heads.
@@ -152,10 +167,11 @@ hipError_t launch_append_rotary(const rbkv_shape& s, const rbkv_batch& b, void* 
 hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                          const void* pool, void* out, float* ws, hipStream_t stream);
 
-// The lean decode as persistent workgroups draining the decode list through a device
-// counter (decode_lean_ok shapes only); the counter must be zero when the first of the
-// launches sharing it starts (launch_decode_claim_reset).  stages: LDS tile stages per
-// workgroup, 1 or 2, for groups of up to four heads (larger groups have one form).
+// The decode as persistent workgroups draining the decode list through a device counter
+// (decode_persistent_ok shapes only); the counter must be zero when the first of the
+// launches sharing it starts (launch_decode_claim_reset).  stages: tile stages per wave
+// of the matrix-core kernel (2 or 3; fewer asks for 2) and per workgroup of the lean
+// kernel at head dim 64 (1 or 2, groups of up to four heads).
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
                                     int32_t workgroups, hipStream_t stream, int stages);

@@ -181,9 +181,9 @@ def test_noalloc_attention_validation():
 def test_workspace_holds_claim_counter_for_overlapped_decodes():
     """bf16 batches with both phases, groups of <= 8 heads and 64-key blocks get a
     256-byte-aligned item counter after the partials (the two-stream call's persistent
-    decodes claim items from it), and so do decode batches at head dim 128 with groups
-    of 2-4 heads (the serial call's decodes are persistent there); other shapes and
-    batches do not."""
+    decodes claim items from it), and so does every decode batch at head dim 128 with
+    groups of 2-16 heads (the matrix-core decode is persistent in the serial call too);
+    other shapes and batches do not."""
     def need(s, n_partials, n_dec, n_pre):
         b = R.Batch()
         b.shape = s
@@ -198,7 +198,7 @@ def test_workspace_holds_claim_counter_for_overlapped_decodes():
     assert need(lean, 0, 7, 2) == 256                # unsplit decodes: the counter alone
     assert need(lean, 5, 7, 0) == part               # no prefill: no overlap, no counter
     assert need(lean, 5, 0, 2) == part
-    # head dim 128, groups of 2-4: the serial call's decodes are persistent too
+    # head dim 128, groups of 2-16: the serial call's decodes are persistent too
     lean128 = shape(block_size=64, head_dim=128)
     part128 = 5 * 2 * (128 + 2) * 4                  # 5200 bytes of partials
     assert need(lean128, 5, 7, 0) == 5376 + 256      # decode-only batch: counter as well
@@ -211,6 +211,14 @@ def test_workspace_holds_claim_counter_for_overlapped_decodes():
     assert need(g8, 5, 7, 2) == 10752 + 256          # 10560 bytes of partials, rounded
     g16 = shape(block_size=64, n_q_heads=32, n_kv_heads=2)       # groups of 16: none
     assert need(g16, 5, 7, 2) == 5 * 16 * (64 + 2) * 4
+    # at head dim 128 groups of 8 and 16 heads decode on the matrix cores: counter in
+    # decode-only batches too; blocks under 64 keys keep the per-item kernels
+    g8_128 = shape(block_size=64, head_dim=128, n_q_heads=16, n_kv_heads=2)
+    assert need(g8_128, 5, 7, 0) == 20992 + 256      # 20800 bytes of partials, rounded
+    g16_128 = shape(block_size=64, head_dim=128, n_q_heads=32, n_kv_heads=2)
+    assert need(g16_128, 5, 7, 2) == 41728 + 256     # 41600 bytes of partials, rounded
+    assert need(g16_128, 5, 7, 0) == 41728 + 256
+    assert need(shape(block_size=32, head_dim=128, n_q_heads=32, n_kv_heads=2), 5, 7, 0) == 41600
 
 
 def test_valid_call_without_gpu_reports_pointer_kind():

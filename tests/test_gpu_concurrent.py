@@ -32,19 +32,21 @@ def _run(wl, concurrent, reps=3):
     return outs
 
 
-@pytest.mark.parametrize("name", ["random_bf16", "random_f32", "lean_g4_d128", "lean_g1_d64",
-                                  "reg_g1_d128",
-                                  "lean_g2_unsplit", "lean_g8_d128", "lean_g6_d64",
-                                  "splitfuse768_gqa4", "full8192_gqa4"])
+@pytest.mark.parametrize("name", ["random_bf16", "random_f32", "mfma_g4_d128", "lean_g1_d64",
+                                  "reg_g1_d128", "mfma_g2_unsplit", "mfma_g8_d128",
+                                  "mfma_g16_d128", "lean_g6_d64", "splitfuse768_gqa4",
+                                  "full8192_gqa4"])
 def test_concurrent_equals_serial(name):
-    """The lean-decode shapes (bf16, groups of up to 8 heads, 64-key blocks) take the
-    overlapped path: persistent decode workgroups on both streams drain one item counter;
-    each item is still computed by one workgroup in the same order, so the bytes match."""
+    """Shapes with a persistent decode (bf16 over 64-key blocks: the matrix-core kernel at
+    head dim 128 for groups of 2-16 heads, the register-only kernel for single heads, the
+    lean kernels at head dim 64) take the overlapped path: persistent decode workgroups on
+    both streams drain one item counter; each item is still computed by one workgroup in
+    the same order, so the bytes match."""
     print(f"concurrent {name}", flush=True)
     if name == "random_bf16":
         wl = W.random_workload(31, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128,
                                block_size=32, n_seqs=8, max_new=90, max_seen=400)
-    elif name == "lean_g4_d128":
+    elif name == "mfma_g4_d128":
         wl = W.random_workload(33, dtype="bf16", n_q_heads=16, n_kv_heads=4, head_dim=128,
                                block_size=64, n_seqs=40, max_new=300, max_seen=3000)
     elif name == "reg_g1_d128":
@@ -53,13 +55,16 @@ def test_concurrent_equals_serial(name):
     elif name == "lean_g1_d64":
         wl = W.random_workload(34, dtype="bf16", n_q_heads=6, n_kv_heads=6, head_dim=64,
                                block_size=128, n_seqs=30, max_new=200, max_seen=2000)
-    elif name == "lean_g8_d128":
+    elif name == "mfma_g8_d128":
         wl = W.random_workload(36, dtype="bf16", n_q_heads=32, n_kv_heads=4, head_dim=128,
                                block_size=64, n_seqs=40, max_new=300, max_seen=3000)
     elif name == "lean_g6_d64":
         wl = W.random_workload(37, dtype="bf16", n_q_heads=12, n_kv_heads=2, head_dim=64,
                                block_size=64, n_seqs=30, max_new=200, max_seen=2500)
-    elif name == "lean_g2_unsplit":
+    elif name == "mfma_g16_d128":
+        wl = W.random_workload(39, dtype="bf16", n_q_heads=32, n_kv_heads=2, head_dim=128,
+                               block_size=128, n_seqs=24, max_new=200, max_seen=3000)
+    elif name == "mfma_g2_unsplit":
         # short histories: every decode is one split, so the workspace holds the counter only
         wl = W.random_workload(35, dtype="bf16", n_q_heads=4, n_kv_heads=2, head_dim=128,
                                block_size=64, n_seqs=12, max_new=70, max_seen=150)

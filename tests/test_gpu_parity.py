@@ -170,11 +170,11 @@ def test_tiny_f32_workload():
 
 @pytest.mark.parametrize("seed", range(19))
 def test_random_small_batches(seed):
-    # Every decode kernel instantiation appears: per-wave (float32; bf16 G <= 4 over blocks
-    # under 64 keys), lean one head per wave (bf16 G <= 4, blocks >= 64; d 64 and 128; its
-    # two-stage form for G 2..4 at d 128: seeds 9, 17, 18),
-    # lean two heads per wave (bf16 G 5..8, blocks >= 64; d 64 and 128) and grouped (bf16
-    # G 9..16, or G 5..8 over blocks under 64 keys).
+    # Every decode kernel appears: per-wave (float32; bf16 G <= 4 over blocks under 64
+    # keys), matrix-core (bf16 d 128, G 2..16, blocks >= 64: seeds 9, 12, 15, 17, 18),
+    # register-only (bf16 d 128, G 1, blocks >= 64: seed 1), lean one head per wave (bf16
+    # d 64, G <= 4, blocks >= 64), lean two heads per wave (bf16 d 64, G 5..8, blocks >=
+    # 64) and grouped (bf16 G 9..16 at d 64, or G 5..16 over blocks under 64 keys).
     combos = [  # dtype, Hq, Hkv, d, bs
         ("bf16", 4, 2, 64, 16), ("bf16", 8, 8, 128, 64), ("f32", 4, 1, 64, 32),
         ("bf16", 14, 2, 128, 32), ("f32", 8, 4, 128, 128), ("bf16", 16, 1, 64, 128),
@@ -234,16 +234,23 @@ def test_long_prefill_chunk_many_tiles():
 
 
 SPLIT_CASES = [  # name, dtype, Hq, Hkv, d, bs, (n_new, seen) per sequence
-    # lean one head per wave, two-stage form (G 4, d 128), one long decode beside a chunk
-    ("lean_g4_d128", "bf16", 8, 2, 128, 64, [(1, 20000), (40, 300), (1, 150), (1, 5000)]),
-    # lean two heads per wave (G 8)
-    ("lean2_g8_d128", "bf16", 16, 2, 128, 64, [(1, 30000), (1, 900), (33, 2000)]),
+    # matrix-core kernel (G 4, d 128), one long decode beside a chunk
+    ("mfma_g4_d128", "bf16", 8, 2, 128, 64, [(1, 20000), (40, 300), (1, 150), (1, 5000)]),
+    # matrix-core kernel (G 8)
+    ("mfma_g8_d128", "bf16", 16, 2, 128, 64, [(1, 30000), (1, 900), (33, 2000)]),
+    # matrix-core kernel (G 12) over 128-key blocks, with items that some waves see no
+    # key of (40 keys) and a one-key decode
+    ("mfma_g12_bs128", "bf16", 24, 2, 128, 128, [(1, 9000), (1, 40), (21, 500), (1, 0)]),
+    # lean two heads per wave (G 8, d 64)
+    ("lean2_g8_d64", "bf16", 16, 2, 64, 64, [(1, 24000), (1, 700), (19, 900)]),
     # lean one head per wave, one stage (G 1, d 64)
     ("lean_g1_d64", "bf16", 2, 2, 64, 128, [(1, 16000), (25, 100), (1, 63)]),
     # register-only kernel (G 1, d 128), with short items a wave sees no key of
     ("reg_g1_d128", "bf16", 4, 4, 128, 64, [(1, 14000), (30, 200), (1, 20), (1, 70)]),
-    # grouped kernel (G 16)
-    ("grouped_g16_d128", "bf16", 32, 2, 128, 64, [(1, 12000), (1, 1), (17, 4000)]),
+    # matrix-core kernel (G 16)
+    ("mfma_g16_d128", "bf16", 32, 2, 128, 64, [(1, 12000), (1, 1), (17, 4000)]),
+    # grouped kernel (G 16, d 64)
+    ("grouped_g16_d64", "bf16", 32, 2, 64, 64, [(1, 12000), (1, 1), (17, 4000)]),
     # per-wave kernel, bf16 over 16-key blocks
     ("perwave_g2_bf16", "bf16", 4, 2, 128, 16, [(1, 9000), (1, 777), (9, 50)]),
     # per-wave kernel, float32
