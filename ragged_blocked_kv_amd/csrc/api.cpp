@@ -393,12 +393,30 @@ rbkv_status check_attention(const rbkv_shape* shape, const rbkv_batch* batch, bo
   return RBKV_OK;
 }
 
+// Mixed batches whose decodes run on the matrix cores take one persistent launch for both
+// phases (launch_mixed): one workgroup per CU, MIXED_DEC_FIRST of every XCD's 32 starting
+// on the decode list.
+constexpr int32_t MIXED_DEC_FIRST = 16;
+bool mixed_launch(const rbkv_shape& s, bool pre, bool dec) {
+  return pre && dec && decode_mfma_ok(s);
+}
+
 // The launches of one attention call on one stream (checks already done).
 rbkv_status launch_attention(const rbkv_shape& s, const rbkv_batch& b, bool pre, bool dec,
                              bool comb, const void* qkv, const void* kv_pool, void* out,
                              void* workspace, hipStream_t hs) {
   hipError_t err = hipSuccess;
-  if (pre) err = launch_prefill(s, b, qkv, kv_pool, out, hs);
+  if (mixed_launch(s, pre, dec)) {
+    int n_cu = 0;
+    int32_t* claims = (int32_t*)((char*)workspace + claim_offset(s, b));
+    err = cu_count(&n_cu);
+    if (err == hipSuccess) err = launch_claims_reset(claims, 9, hs);
+    if (err == hipSuccess)
+      err = launch_mixed(s, b, qkv, kv_pool, out, (float*)workspace, claims, n_cu,
+                         MIXED_DEC_FIRST, hs);
+    pre = dec = false;
+  }
+  if (err == hipSuccess && pre) err = launch_prefill(s, b, qkv, kv_pool, out, hs);
   if (err == hipSuccess && dec) {
     if (serial_persistent(s)) {
       int n_cu = 0;
@@ -702,6 +720,11 @@ rbkv_status ragged_blocked_attention_concurrent(const rbkv_shape* shape, const r
   if (st != RBKV_OK || !launch) return st;
   hipStream_t hs = (hipStream_t)stream, hside = (hipStream_t)side_stream;
   hipEvent_t fork = (hipEvent_t)fork_event, join = (hipEvent_t)join_event;
+  // Batches that take the mixed launch run it on the caller's stream (the two phases
+  // already share the chip inside it).
+  if (mixed_launch(*shape, pre, dec))
+    return launch_attention(*shape, *batch, pre, dec, batch->n_combine_items > 0, qkv, kv_pool,
+                            out, workspace, hs);
   if (uses_claim(*shape, *batch))
     return attention_overlapped(*shape, *batch, qkv, kv_pool, out, (char*)workspace, hs, hside,
                                 fork, join);

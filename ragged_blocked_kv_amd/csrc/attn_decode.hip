@@ -16,6 +16,7 @@
 // DeepSpeed-MII", section 10.3.
 #include <algorithm>
 
+#include "decode_mfma.h"
 #include "rbkv_device.h"
 #include "rbkv_internal.h"
 
@@ -24,9 +25,6 @@ namespace {
 
 // K/V tile rows are read once per work item: non-temporal loads (measured 4-7% faster
 // decode than plain loads on the MHA, SplitFuse and full-budget batches).
-typedef short s16x4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4v lds_s16x4v;
-
 __device__ __forceinline__ u32x4 ldnt(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
@@ -1155,26 +1153,10 @@ void decode_reg_kernel(
   }  // items
 }
 
-// Decode on the matrix cores for bf16 caches at head dim 128 over blocks of at least 64
-// keys, for groups of up to 16 query heads.  The four wavefronts of a workgroup each take
-// 16 keys of every 64-key tile of the item and run their own pipeline with no workgroup
-// barrier: the wave's K and V rows go from HBM straight into its own LDS slices
-// (global_load_lds_dwordx4, ST stages, the next tile in flight while this one is computed).
-// Per tile and wave:
-//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over four 32-dim steps: rows are the wave's 16
-//                   keys, columns the group's query heads (columns past G repeat the last
-//                   head), K fragments from LDS, Q^T in registers for the whole item;
-//   online softmax  lane (g, j) holds the scores of keys 4g..4g+3 for head j, so the
-//                   running maximum of head j is lane-local once the four lane groups
-//                   agree; it moves only past a slack of 2^8 (a cross-lane max when a lane
-//                   asks for it), and the weights are rounded to bf16 as they are summed;
-//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16 per 16-dim block: the weights are already in
-//                   the operand layout (the S^T accumulator layout), V^T fragments come from
-//                   transposing LDS reads (ds_read_b64_tr_b16).
-// K slices carry the XOR swizzle chunk ^ key % 16 (fragment reads hit 16 distinct bank
-// groups), V slices chunk ^ 2 (key % 8) (each half-wave of a transposing read covers 64
-// banks).  At the end of the item each wave leaves its unnormalised output in its own LDS
-// region and the four are merged like split-K partials.
+// Decode on the matrix cores (bf16, head dim 128, blocks of 64+ keys, groups of up to 16
+// heads): four wavefronts per workgroup, each streaming a 16-key slice of every 64-key
+// step through its own LDS stages (mfma_decode::run_item).  With a claim counter the
+// workgroups are persistent and take items from it.
 template <int ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(
@@ -1184,188 +1166,19 @@ void decode_mfma_kernel(
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
     int32_t Hkv, int32_t G, int32_t bs, int32_t split_tiles, float scale_log2,
     int32_t* __restrict__ claim, int32_t n_items) {
-  constexpr int D = 128, NW = 4, NT = NW * 64;
-  constexpr int TE = 16 * D;       // elements of a wave's K (or V) slice of one tile
-  constexpr int RS = D + 4;        // row stride (floats) of a wave's output in the merge
-  constexpr float SLACK = 8.f;
-  static_assert(ST >= 2 && ST <= 3, "stages");
-  static_assert(16 * RS * 4 <= ST * 2 * TE * 2, "merge rows fit the wave's region");
-  __shared__ __attribute__((aligned(16))) uint16_t buf[NW][ST][2 * TE];
-  __shared__ float ml[NW][16][2];
+  __shared__ __attribute__((aligned(16))) uint16_t buf[mfma_decode::buf_elems<ST, 4>()];
+  __shared__ float ml[mfma_decode::ml_floats<4>()];
   __shared__ int32_t claimed;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, j = lane & 15;
-
   auto next_item = [&]() -> int32_t {
     __syncthreads();  // the previous item's merge is read by every wave
-    if (tid == 0) claimed = atomicAdd(claim, 1);
+    if (threadIdx.x == 0) claimed = atomicAdd(claim, 1);
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(claimed);
   };
-
-  // Loader: instruction n of a slice writes LDS bytes 1024n + 16 lane, i.e. key 4n + g,
-  // chunk slot j; the source chunk is chosen so the slot carries the swizzle.
-  uint32_t ld_k[4], ld_v[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int key = 4 * n + g;
-    ld_k[n] = (uint32_t)((j ^ (key & 15)) * 16);
-    ld_v[n] = (uint32_t)((j ^ (2 * (key & 7))) * 16);
-  }
-  // K fragment of step s for key j: chunk 4s + g.  V^T fragment of dim block d: source
-  // lane (g, a, r) (a = lane / 4 % 4, r = lane % 4) reads key 4g + a, dims 16d + 4r .. +3.
-  uint32_t kfo[4], vfo[8];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) kfo[s] = (uint32_t)(j * D + (((4 * s + g) ^ j) * 8));
-  {
-    const int a = (lane >> 2) & 3, r = lane & 3, key = 4 * g + a;
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-      vfo[d] = (uint32_t)(TE + key * D + ((2 * d + (r >> 1)) ^ (2 * (key & 7))) * 8 + (r & 1) * 4);
-  }
-  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(&buf[wave][0][0]));
-
   for (int32_t item = claim ? next_item() : (int32_t)blockIdx.x; item < n_items;
-       item = claim ? next_item() : n_items) {
-    const int4 w = work[item];
-    const int32_t token = w.x, kvh = w.y, split = w.z, slot = w.w;
-    const int32_t seq = tok2seq[token];
-    const int32_t nkeys = pos[token] + 1;
-    const int32_t tiles_total = (nkeys + 63) >> 6;
-    const int32_t t_begin = slot < 0 ? 0 : split * split_tiles;
-    const int32_t t_end = slot < 0 ? tiles_total : min(tiles_total, t_begin + split_tiles);
-    const int32_t key_end = min(nkeys, t_end * 64);
-    const int32_t* bids = block_ids + block_off[seq];
-    const int bsh = 31 - __builtin_clz(bs);
-    const size_t head_stride = (size_t)bs * D;
-    const size_t blk_stride = (size_t)2 * Hkv * head_stride;
-    const uint32_t v_bytes = (uint32_t)(Hkv * head_stride * 2);
-    const uint16_t* pool_g = pool + (size_t)kvh * head_stride;
-
-    // The wave's 16 keys of tile t into stage st.  A tile lies in one block (blocks hold
-    // at least 64 keys); rows past the end of the split load its last key, whose weight is 0.
-    auto issue = [&](int32_t t, int st) {
-      const int32_t key0 = t * 64;
-      const uint16_t* base = pool_g + (size_t)bids[key0 >> bsh] * blk_stride + (size_t)(key0 & (bs - 1)) * D;
-      const int32_t rmax = key_end - 1 - key0;
-      const uint32_t dst = lds_wave + (uint32_t)st * (2 * TE * 2);
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint32_t roff = (uint32_t)min(16 * wave + 4 * n + g, rmax) * (D * 2);
-        load_lds16_nt_s(base, roff + ld_k[n], dst + n * 1024);
-        load_lds16_nt_s(base, v_bytes + roff + ld_v[n], dst + TE * 2 + n * 1024);
-      }
-    };
-
-    u32x4 qb[4];
-    float m = -1e30f, l = 0.f;  // finite start: a wave may see no valid key of a short item
-    f32x4 o[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](int32_t t, int st) {
-      const uint16_t* kt = &buf[wave][st][0];
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 kf = *(const u32x4*)(kt + kfo[s]);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, kf),
-                                                       __builtin_bit_cast(bf16x8v, qb[s]), sacc, 0, 0, 0);
-      }
-      const int32_t k0 = t * 64 + 16 * wave + 4 * g;
-      float sc[4], mt = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] = k0 + i < key_end ? sacc[i] * scale_log2 : -INFINITY;
-        mt = fmaxf(mt, sc[i]);
-      }
-      if (__any(mt > m + SLACK)) {
-        float M = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        M = fmaxf(M, __shfl_xor(M, 32, 64));
-        const float mnew = M > m + SLACK ? M : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] *= alpha;
-        m = mnew;
-      }
-      const uint32_t p01 = pack_bf16x2(__builtin_amdgcn_exp2f(sc[0] - m), __builtin_amdgcn_exp2f(sc[1] - m));
-      const uint32_t p23 = pack_bf16x2(__builtin_amdgcn_exp2f(sc[2] - m), __builtin_amdgcn_exp2f(sc[3] - m));
-      l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p01), as_bf16x2(0x3f803f80u), l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p23), as_bf16x2(0x3f803f80u), l, false);
-      const s16x4v pb = __builtin_bit_cast(s16x4v, u32x2{p01, p23});
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const s16x4v vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(kt + vfo[d]));
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pb, o[d], 0, 0, 0);
-      }
-    };
-
-    // The wave's own pipeline: the item's first ST tiles go out at once, then each tile's
-    // stage is refilled with the tile ST further as soon as it has been computed; before a
-    // tile is read only the loads of later tiles (8 per tile) may be outstanding.
-#pragma unroll
-    for (int u = 0; u < ST; ++u)
-      if (t_begin + u < t_end) issue(t_begin + u, u);
-    // Q^T operand of step s: head j (clamped to the group), dims 32s + 8g .. +8.  The
-    // empty asm makes the compiler complete these loads here (together with the first
-    // tiles, which are needed first anyway), so that no wait it tracks for them falls
-    // inside the tile loop, where it would also drain the next tiles' loads.
-    {
-      const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + min(j, G - 1)) * D;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qb[s] = ld16(qrow + (4 * s + g) * 8);
-      asm volatile("" : : "v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
-    }
-    int st = 0;
-    for (int32_t t = t_begin; t < t_end; ++t) {
-      const int32_t later = min(t_end - 1 - t, ST - 1);
-      if (ST == 3 && later >= 2) wait_vmcnt<16>();
-      else if (later >= 1) wait_vmcnt<8>();
-      else wait_vmcnt<0>();
-      compute(t, st);
-      if (t + ST < t_end) issue(t + ST, st);
-      st = st + 1 == ST ? 0 : st + 1;
-    }
-
-    // Merge: each wave's weight sum over its lane groups, then the four waves through LDS.
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    float* ro = (float*)&buf[wave][0][0];  // this wave's region: its reads of it are done
-    if (j < G) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) *(f32x4*)(ro + j * RS + 16 * d + 4 * g) = o[d];
-      if (g == 0) {
-        ml[wave][j][0] = m;
-        ml[wave][j][1] = l;
-      }
-    }
-    __syncthreads();
-    for (int u = tid; u < G * D; u += NT) {
-      const int h = u / D, dim = u % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, ml[wv][h][0]);
-      float num = 0.f, den = 0.f;
-#pragma unroll
-      for (int wv = 0; wv < NW; ++wv) {
-        const float a = __builtin_amdgcn_exp2f(ml[wv][h][0] - M);
-        num = fmaf(a, ((const float*)&buf[wv][0][0])[h * RS + dim], num);
-        den = fmaf(a, ml[wv][h][1], den);
-      }
-      if (slot < 0) {
-        out[((size_t)token * Hq + (size_t)kvh * G + h) * D + dim] = (uint16_t)bf16_rne_f32(num / den);
-      } else {
-        float* part = ws + (size_t)slot * G * (D + 2);
-        if (dim == 0) {
-          part[h] = M;
-          part[G + h] = den;
-        }
-        part[2 * G + (size_t)h * D + dim] = num;
-      }
-    }
-    if (!claim) break;
-  }  // items
+       item = claim ? next_item() : n_items)
+    mfma_decode::run_item<ST, 4>(qkv, pool, out, ws, work, tok2seq, pos, block_off, block_ids, Hq,
+                                 Hkv, G, bs, split_tiles, scale_log2, item, buf, ml);
 }
 
 template <int ST>
@@ -1430,6 +1243,11 @@ hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv
 
 __global__ void lean_claim_reset_kernel(int32_t* claim) {
   __hip_atomic_store(claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void claims_reset_kernel(int32_t* claims, int n) {
+  if ((int)threadIdx.x < n)
+    __hip_atomic_store(claims + threadIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int NW>
@@ -1501,6 +1319,12 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
 }
 
 }  // namespace
+
+hipError_t launch_claims_reset(int32_t* claims, int n, hipStream_t stream) {
+  if (n < 1 || n > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(claims_reset_kernel, dim3(1), dim3(64), 0, stream, claims, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream) {
   hipLaunchKernelGGL(lean_claim_reset_kernel, dim3(1), dim3(1), 0, stream, claim);

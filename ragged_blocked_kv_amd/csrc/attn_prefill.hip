@@ -29,6 +29,7 @@
 // "DeepSpeed-Inference and DeepSpeed-MII", sections 10.3 and 10.10; query-tile sizing per
 // head and blocked attention over work atoms: "DeepSpeed Inference v2 source tour",
 // section "Ragged batches: packing a whole server into four tensors".
+#include "decode_mfma.h"
 #include "rbkv_device.h"
 #include "rbkv_internal.h"
 
@@ -80,13 +81,19 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// One work item (kv group gidx = (sequence, kv head), query tile jq of the sequence's nqt)
+// by the whole workgroup, with Ks / Vs the STAGES-tile K and V rings in LDS.  Every thread
+// of the workgroup calls it; it ends with every wave past its last barrier.  The pointers
+// must be the calling kernel's own restrict parameters (the block ids are read through
+// the scalar cache).
 template <int D>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
+__device__ __forceinline__ void prefill_item(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
-    uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_groups, int32_t nq_max,
-    int32_t qtt, const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
-    const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
-    int32_t Hkv, int32_t G, int32_t bs, float scale_log2) {
+    uint16_t* __restrict__ out, int32_t qtt, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ seen_arr, const int32_t* __restrict__ block_off,
+    const int32_t* __restrict__ block_ids, int32_t Hq, int32_t Hkv, int32_t G, int32_t bs,
+    float scale_log2, uint16_t (*Ks)[64 * D], uint16_t (*Vs)[64 * D], int32_t gidx,
+    int32_t seq, int32_t nqt, int32_t jq) {
   constexpr int CPR = D / 8;                   // 16-byte chunks per key row
   constexpr int TILE_CHUNKS = 64 * CPR;        // chunks per K (or V) tile
   constexpr int LOADERS = PF_THREADS / 2;      // threads of the loading group
@@ -97,21 +104,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   constexpr int DB = D / 32;                   // 32-wide dim blocks of the output
   constexpr int MAXNB = 4;                     // blocks a 64-key tile can span (block size 16)
   static_assert(NLD >= 1 && ROWS_PER_LD % 16 == 0, "loader geometry");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[STAGES][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[STAGES][64 * D];
-
-  // Work placement.  Block b runs on XCD b % 8.  The (sequence, kv head) groups, in the
-  // order of the ranked chunk sequences (longest first), are dealt round-robin over the
-  // XCDs, so each XCD gets an even share; the query tiles of one group run back to back
-  // on one XCD (longest tile first) and share its L2.  Slots past a group's tiles exit.
-  const int32_t xcd = (int32_t)(blockIdx.x % N_XCD);
-  const int32_t k = (int32_t)(blockIdx.x / N_XCD);
-  const int32_t gidx = (k / nq_max) * N_XCD + xcd;
-  if (gidx >= n_groups) return;  // whole workgroup leaves together
-  const int4 rec = work[gidx / Hkv];
-  const int32_t seq = rec.x, nqt = rec.y;
-  const int32_t jq = k % nq_max;
-  if (jq >= nqt) return;
   const int32_t kvh = gidx % Hkv;
   const int32_t qt = nqt - 1 - jq;
   const int32_t q0 = qt * qtt;
@@ -433,6 +425,94 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
     }
 }
 
+// Work placement.  Block b runs on XCD b % 8.  The (sequence, kv head) groups, in the
+// order of the ranked chunk sequences (longest first), are dealt round-robin over the
+// XCDs, so each XCD gets an even share; the query tiles of one group run back to back on
+// one XCD (longest tile first) and share its L2.  Slots past a group's tiles exit.
+template <int D>
+__global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
+    uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_groups, int32_t nq_max,
+    int32_t qtt, const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
+    const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
+    int32_t Hkv, int32_t G, int32_t bs, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[STAGES][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[STAGES][64 * D];
+  const int32_t xcd = (int32_t)(blockIdx.x % N_XCD);
+  const int32_t k = (int32_t)(blockIdx.x / N_XCD);
+  const int32_t gidx = (k / nq_max) * N_XCD + xcd;
+  if (gidx >= n_groups) return;  // whole workgroup leaves together
+  const int4 rec = work[gidx / Hkv];
+  const int32_t seq = rec.x, nqt = rec.y;
+  const int32_t jq = k % nq_max;
+  if (jq >= nqt) return;
+  prefill_item<D>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv, G, bs,
+                  scale_log2, Ks, Vs, gidx, seq, nqt, jq);
+}
+
+// Mixed batches (bf16, head dim 128, groups of 2-16 heads, blocks of 64+ keys): one
+// persistent workgroup per CU takes items from both work lists, so the two phases share
+// the chip by CUs inside one launch.  A workgroup starts on the decode list if it is one of
+// the first dec_first of its XCD (block b runs on XCD b % 8), on the prefill list
+// otherwise, and moves to the other list when its own is exhausted; it leaves when both
+// are.  Prefill items come from per-XCD lists (the placement of prefill_attn_kernel, with
+// a counter per XCD in claims[1 + xcd]; an XCD whose list is exhausted takes items from
+// the next ones), decode items from one list (claims[0]), eight wavefronts per item
+// (mfma_decode::run_item, two stages).  The ring of the prefill and the stages of the
+// decode share the LDS.  claims[0..8] must be zero at launch.
+__global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
+    uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ pwork,
+    int32_t n_groups, int32_t nq_max, int32_t qtt, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ seen_arr, const int4* __restrict__ dwork,
+    const int32_t* __restrict__ tok2seq, const int32_t* __restrict__ pos, int32_t n_dec,
+    int32_t split_tiles, const int32_t* __restrict__ block_off,
+    const int32_t* __restrict__ block_ids, int32_t Hq, int32_t Hkv, int32_t G, int32_t bs,
+    float scale_log2, int32_t* __restrict__ claims, int32_t dec_first) {
+  constexpr int D = 128;
+  constexpr int RING = STAGES * 64 * D;  // elements of the prefill's K (or V) ring
+  static_assert(mfma_decode::buf_elems<2, PF_WAVES>() <= 2 * RING, "decode stages fit the ring");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * RING];
+  __shared__ float ml[mfma_decode::ml_floats<PF_WAVES>()];
+  __shared__ int32_t claimed;
+  uint16_t(*Ks)[64 * D] = (uint16_t(*)[64 * D])lds;
+  uint16_t(*Vs)[64 * D] = (uint16_t(*)[64 * D])(lds + RING);
+  // XCD this workgroup runs on (hardware register XCC_ID, bits 0-3).
+  const int32_t home = (int32_t)(__builtin_amdgcn_s_getreg(20 | (3 << 11)) & (N_XCD - 1));
+  bool dec = (int32_t)(blockIdx.x / N_XCD) < dec_first;
+  bool pre_left = n_groups > 0, dec_left = n_dec > 0;
+  int32_t xoff = 0;  // prefill list being drained: XCD home + xoff
+  while (pre_left || dec_left) {
+    if (!pre_left) dec = true;
+    if (!dec_left) dec = false;
+    const int32_t xcd = (home + xoff) & (N_XCD - 1);
+    __syncthreads();  // the previous item is done with the LDS and the claim word
+    if (threadIdx.x == 0) claimed = atomicAdd(dec ? &claims[0] : &claims[1 + xcd], 1);
+    __syncthreads();
+    const int32_t c = __builtin_amdgcn_readfirstlane(claimed);
+    if (dec) {
+      if (c >= n_dec) {
+        dec_left = false;
+        continue;
+      }
+      mfma_decode::run_item<2, PF_WAVES>(qkv, pool, out, ws, dwork, tok2seq, pos, block_off,
+                                         block_ids, Hq, Hkv, G, bs, split_tiles, scale_log2, c,
+                                         lds, ml);
+    } else {
+      const int32_t gidx = (c / nq_max) * N_XCD + xcd;
+      if (gidx >= n_groups) {
+        if (++xoff == N_XCD) pre_left = false;
+        continue;
+      }
+      const int4 rec = pwork[gidx / Hkv];
+      const int32_t jq = c % nq_max;
+      if (jq >= rec.y) continue;
+      prefill_item<D>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv, G, bs,
+                      scale_log2, Ks, Vs, gidx, rec.x, rec.y, jq);
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
                     void* out, hipStream_t stream) {
@@ -450,6 +530,22 @@ hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
 }
 
 }  // namespace
+
+hipError_t launch_mixed(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                        const void* pool, void* out, float* ws, int32_t* claims,
+                        int32_t workgroups, int32_t dec_first, hipStream_t stream) {
+  if (!decode_mfma_ok(s)) return hipErrorInvalidValue;
+  const float scale_log2 = 1.4426950408889634f / sqrtf(128.f);
+  const int32_t G = s.n_q_heads / s.n_kv_heads;
+  hipLaunchKernelGGL(mixed_attn_kernel, dim3(workgroups), dim3(PF_THREADS), 0, stream,
+                     (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out, ws,
+                     (const int4*)b.prefill_work, b.n_prefill_seqs * s.n_kv_heads,
+                     b.prefill_qtiles_max, q_tile_tokens(G), b.cu_seqlens, b.seen,
+                     (const int4*)b.decode_work, b.token_to_seq, b.pos, b.n_decode_items,
+                     b.split_tiles, b.block_offsets, b.block_ids, s.n_q_heads, s.n_kv_heads, G,
+                     s.block_size, scale_log2, claims, dec_first);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                           const void* pool, void* out, hipStream_t stream) {

@@ -180,6 +180,15 @@ hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream);
 hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                           const void* pool, void* out, hipStream_t stream);
 
+// Prefill and decode items of a mixed batch in one launch of `workgroups` persistent
+// workgroups (decode_mfma_ok shapes; one workgroup fits a CU), dec_first of every XCD's
+// starting on the decode list; claims[0..8] zero at launch (launch_claims_reset).
+hipError_t launch_mixed(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
+                        const void* pool, void* out, float* ws, int32_t* claims,
+                        int32_t workgroups, int32_t dec_first, hipStream_t stream);
+// Zeroes n (<= 64) item counters.
+hipError_t launch_claims_reset(int32_t* claims, int n, hipStream_t stream);
+
 hipError_t launch_combine(const rbkv_shape& s, const rbkv_batch& b, const float* ws,
                           void* out, hipStream_t stream);
 
