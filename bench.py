@@ -3,10 +3,14 @@
 A step is one pass over one batch with every input already resident in HBM: the device
 metadata build (``ragged_batch_rebuild``), the rotary append
 (``blocked_kv_append_rotary``) and the attention.  The timed steps run the attention as
-``ragged_blocked_attention_concurrent`` (prefill chunks and decodes sharing the chip on
-two streams, bit-identical output); a second, serial pass issues its prefill, decode and
-combine phases one after another so that each kernel is timed with HIP events on the
-stream it runs on (the roofline and the phase breakdown).  The batch is the full-budget mixed batch: 8192 new tokens over
+``ragged_blocked_attention_concurrent``: for bf16 batches at head dim 128 with groups of
+2-16 heads, one launch of persistent workgroups that take prefill tiles and decode
+items from the same chip (the mixed launch, then the split-K combine); for other shapes
+the chunks and the decodes on two streams.  A second pass times the mixed launch alone
+(``RBKV_PHASE_ATTEND``) with HIP events on its stream (the roofline of the step's
+dominant kernel), and a serial pass issues the prefill, decode and combine phases as
+separate launches one after another, so that each kernel is timed on its own (their
+rooflines and the phase breakdown).  The batch is the full-budget mixed batch: 8192 new tokens over
 256 sequences (16 prefill chunks of 256..512 tokens and 240 decodes, seen ~ U[0, 8192]),
 GQA 32 query / 8 kv heads, head dim 128, 64-token blocks, bf16.  The host half of
 ``ragged_batch_finalize`` (validation, packing, the small host-to-device upload) runs once
@@ -64,9 +68,12 @@ def source_tokens_digest(text):
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def kernel_source_digest(name):
-    p = os.path.join(ROOT, "ragged_blocked_kv_amd", "csrc", name)
-    return source_tokens_digest(open(p).read())
+def kernel_source_digest(names):
+    """Digest of the sources a kernel group is built from (one name or a tuple)."""
+    if isinstance(names, str):
+        names = (names,)
+    return source_tokens_digest("".join(
+        open(os.path.join(ROOT, "ragged_blocked_kv_amd", "csrc", n)).read() for n in names))
 
 
 def measured_traffic(label, workload):
@@ -88,9 +95,10 @@ def measured_traffic(label, workload):
 # name fragments).  A label's record is valid while its source file hashes the same.
 KERNEL_GROUPS = {
     "attn_prefill.hip": ("attn_prefill.hip", ("prefill_attn_kernel",)),
-    "attn_decode.hip": ("attn_decode.hip", ("decode_attn_kernel", "decode_group_kernel",
-                                            "decode_lean_kernel", "decode_lean2_kernel",
-                                            "decode_reg_kernel", "decode_mfma_kernel")),
+    "attn_prefill.hip/mixed": (("attn_prefill.hip", "decode_mfma.h"), ("mixed_attn_kernel",)),
+    "attn_decode.hip": (("attn_decode.hip", "decode_mfma.h"),
+                        ("decode_attn_kernel", "decode_group_kernel", "decode_lean_kernel",
+                         "decode_lean2_kernel", "decode_reg_kernel", "decode_mfma_kernel")),
     "append_rotary.hip": ("append_rotary.hip", ("append_rotary_kernel",)),
     "attn_combine.hip": ("attn_combine.hip", ("combine_kernel",)),
     "meta_build.hip": ("meta_build.hip", ("meta_build_kernel",)),
@@ -115,6 +123,14 @@ def decode_kernel_name(wl):
     if wl.dtype == "bf16" and g > 4:
         return "decode_group_kernel"
     return "decode_attn_kernel"
+
+
+def mixed_launch(wl):
+    """Whether the library runs this batch's attention as one mixed launch (prefill tiles
+    and decode items from one set of persistent workgroups)."""
+    g = wl.n_q_heads // wl.n_kv_heads
+    return (wl.dtype == "bf16" and wl.head_dim == 128 and wl.block_size >= 64 and 2 <= g <= 16
+            and bool((wl.n_new > 1).any()) and bool((wl.n_new == 1).any()))
 
 
 def copy_calibration(nbytes, reps):
@@ -409,8 +425,8 @@ def serving_leg(wl, eng, qkv, pool, out, stream, passes=12, warm=3):
     """A Dynamic SplitFuse serving loop on the bench's shapes, end to end per pass:
     compose the batch on the native ledger (the decodes of the batch's single-token
     sequences first, then a seeded queue of prompts of 256..4096 tokens cut to fill the
-    8192-token budget), put, finalize from the ledger, rotary append, attention (the
-    two-stream call),
+    8192-token budget), put, finalize from the ledger, rotary append, attention (one
+    ragged_blocked_attention_concurrent call),
     synchronize (a serving loop needs the pass's output before composing the next one)
     and post_forward.  Finished prompts are flushed; decodes run on.  Times are medians
     over the timed passes."""
@@ -613,14 +629,16 @@ def measured_mfma(label, workload):
                                 "dispatches") if k in rec}
 
 
-def time_steps(wl, eng, qkv, pool, out, stream, steps, warmup, two_stream=True):
-    """Serial steps (metadata rebuild, append, prefill, decode, combine) with HIP events
-    between the phases on the stream they run on, then (``two_stream``) steps with the
-    attention as the two-stream call and events around it.  Both bracketed by
-    synchronisations; wall-clock seconds of each loop and the per-step event times."""
+def time_steps(wl, eng, qkv, pool, out, stream, steps, warmup, one_call=True):
+    """Serial steps (metadata rebuild, append, prefill, decode, combine as separate
+    launches) with HIP events between the phases on the stream they run on, then
+    (``one_call``) steps with the attention as one ragged_blocked_attention_concurrent
+    call and events around it, and, for batches it runs as the mixed launch, that launch
+    alone (RBKV_PHASE_ATTEND) between events.  Each loop bracketed by synchronisations;
+    wall-clock seconds of the step loops and the per-step event times."""
     import torch
 
-    from ragged_blocked_kv_amd import PHASE_COMBINE, PHASE_DECODE, PHASE_PREFILL
+    from ragged_blocked_kv_amd import PHASE_ATTEND, PHASE_COMBINE, PHASE_DECODE, PHASE_PREFILL
 
     def step(ev=None):
         def mark(k):
@@ -649,7 +667,7 @@ def time_steps(wl, eng, qkv, pool, out, stream, steps, warmup, two_stream=True):
     wall_serial = time.perf_counter() - t0
 
     # The same work with the prefill and the decodes sharing the chip
-    # (ragged_blocked_attention_concurrent, bit-identical output).
+    # (ragged_blocked_attention_concurrent).
     def step_concurrent(ev=None):
         eng.rebuild(stream=stream)
         eng.append_rotary(qkv, pool, wl.rope_base, stream=stream)
@@ -659,8 +677,8 @@ def time_steps(wl, eng, qkv, pool, out, stream, steps, warmup, two_stream=True):
         if ev is not None:
             ev[1].record(stream)  # after the join: both streams' work is done
 
-    wall, ts = None, None
-    if two_stream:
+    wall, ts, mixed = None, None, None
+    if one_call:
         for _ in range(warmup):
             step_concurrent()
         cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
@@ -671,20 +689,29 @@ def time_steps(wl, eng, qkv, pool, out, stream, steps, warmup, two_stream=True):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ts = np.array([cev[k][0].elapsed_time(cev[k][1]) for k in range(steps)])
+    if one_call and mixed_launch(wl):
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            mev[k][0].record(stream)
+            eng.attention_phase(PHASE_ATTEND, qkv, pool, out, stream=stream)
+            mev[k][1].record(stream)
+        torch.cuda.synchronize()
+        mixed = np.array([mev[k][0].elapsed_time(mev[k][1]) for k in range(steps)])
     return {
         "phase_ms": {p: float(np.mean([events[k][j].elapsed_time(events[k][j + 1])
                                        for k in range(steps)]))
                      for j, p in enumerate(PHASES)},
         "step_ms": np.array([events[k][0].elapsed_time(events[k][5]) for k in range(steps)]),
         "attn_ms": np.array([events[k][2].elapsed_time(events[k][5]) for k in range(steps)]),
-        "two_stream_ms": ts, "wall_serial": wall_serial, "wall_two_stream": wall,
+        "call_ms": ts, "mixed_ms": mixed, "wall_serial": wall_serial, "wall_call": wall,
     }
 
 
 def figures(wl, tm):
     """The per-configuration figures: attention tokens/s and whole-attention HBM
-    fraction (serial phases and the two-stream call), each dominant kernel against its
-    own peak, append and combine."""
+    fraction (separate launches one after another, and the one-call attention), each
+    kernel against its own peak (the mixed launch, the prefill and decode kernels of the
+    separate launches), append and combine."""
     work = algorithmic_work(wl)
     ph = tm["phase_ms"]
     pct = lambda a: [round(float(np.percentile(a, q)) * 1e3, 1) for q in (10, 50, 90)]
@@ -697,11 +724,20 @@ def figures(wl, tm):
 
     serial_ms = ph["prefill"] + ph["decode"] + ph["combine"]
     att = {"bytes": work["attention_bytes"], "serial": attention(serial_ms, tm["attn_ms"]),
-           "two_stream": None}
-    if tm["two_stream_ms"] is not None:
-        att["two_stream"] = attention(float(np.median(tm["two_stream_ms"])), tm["two_stream_ms"])
-    att["timed_call"] = "two-stream" if att["two_stream"] else "serial"
-    att["hbm_frac"] = (att["two_stream"] or att["serial"])["hbm_frac_attention"]
+           "call": None}
+    if tm["call_ms"] is not None:
+        att["call"] = attention(float(np.median(tm["call_ms"])), tm["call_ms"])
+    att["timed_call"] = ("serial" if att["call"] is None else
+                         "mixed launch" if mixed_launch(wl) else "two streams")
+    att["hbm_frac"] = (att["call"] or att["serial"])["hbm_frac_attention"]
+    mixed = None
+    if tm.get("mixed_ms") is not None:
+        us = float(np.mean(tm["mixed_ms"])) * 1e3
+        gbs = work["attention_bytes"] / (us * 1e-6) / 1e9
+        mixed = {"kernel": "mixed_attn_kernel", "us": round(us, 2),
+                 "us_p10_p50_p90": pct(tm["mixed_ms"]), "bytes": work["attention_bytes"],
+                 "flops": work["prefill_flops"], "GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                 "mfma_frac": work["prefill_flops"] / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS}
     dec = pre = None
     # float32 batches run every item (chunks too) on the vector-ALU decode kernel
     dec_bytes = work["decode_bytes"] if wl.dtype == "bf16" else work["attention_bytes"]
@@ -718,6 +754,7 @@ def figures(wl, tm):
     return {
         "S": wl.S, "T": wl.T, "dtype": wl.dtype,
         "attention": att,
+        "mixed": mixed,
         "decode": dec,
         "prefill": pre,
         "append": {"us": round(ph["append"] * 1e3, 2), "bytes": work["append_bytes"],
@@ -843,7 +880,7 @@ def main():
                 else blk.numpy()
 
     tm = time_steps(wl, eng, qkv, pool, out, stream, args.steps, args.warmup,
-                    two_stream=not args.serial_only)
+                    one_call=not args.serial_only)
 
     # Dynamic SplitFuse serving loop (rewrites the metadata and pool slots, so it runs
     # after the timed steps and after the CPU-baseline history has been copied).
@@ -853,9 +890,28 @@ def main():
 
     fig = figures(wl, tm)
     phase_ms = tm["phase_ms"]
-    wall = tm["wall_two_stream"] if tm["wall_two_stream"] is not None else tm["wall_serial"]
+    wall = tm["wall_call"] if tm["wall_call"] is not None else tm["wall_serial"]
     ms_per_step = wall * 1e3 / args.steps
-    if fig["prefill"] and (not fig["decode"] or phase_ms["prefill"] >= phase_ms["decode"]):
+    if fig["mixed"]:
+        # The timed step's dominant kernel does the whole attention: its HBM bound
+        # (every K/V row, Q and output once at 8 TB/s) exceeds its matrix-core bound.
+        mx = fig["mixed"]
+        roof = {"kernel": mx["kernel"], "bound": "hbm", "achieved": mx["GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": mx["hbm_frac"],
+                "traffic": measured_traffic("attn_prefill.hip/mixed", wl.name),
+                "per_launch": {"bytes": mx["bytes"], "flops": mx["flops"], "us": mx["us"]},
+                "mfma_frac": mx["mfma_frac"]}
+        if fig["decode"]:
+            dc = fig["decode"]
+            roof["decode_kernel"] = {"kernel": dc["kernel"], "us": dc["us"], "GBs": dc["GBs"],
+                                     "frac": dc["hbm_frac"],
+                                     "traffic": measured_traffic("attn_decode.hip", wl.name)}
+        if fig["prefill"]:
+            pf = fig["prefill"]
+            roof["prefill_kernel"] = {"kernel": pf["kernel"], "us": pf["us"],
+                                      "TFLOPs": pf["TFLOPs"], "frac": pf["mfma_frac"],
+                                      "traffic": measured_traffic("attn_prefill.hip", wl.name)}
+    elif fig["prefill"] and (not fig["decode"] or phase_ms["prefill"] >= phase_ms["decode"]):
         pf = fig["prefill"]
         roof = {"kernel": "prefill_attn_kernel", "bound": "mfma", "achieved": pf["TFLOPs"],
                 "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": pf["mfma_frac"],
@@ -912,6 +968,9 @@ def main():
             "kv_pool_blocks": wl.num_blocks,
             "step": "metadata rebuild + rotary append + attention (prefill, decode, combine "
                     "one after another)" if args.serial_only else
+                    "metadata rebuild + rotary append + attention (prefill tiles and decode "
+                    "items from one launch of persistent workgroups, then the split-K combine)"
+                    if mixed_launch(wl) else
                     "metadata rebuild + rotary append + attention (prefill chunks and decodes "
                     "sharing the chip on two streams, then the split-K combine)",
         },
@@ -921,7 +980,7 @@ def main():
         "attention_only": fig["attention"]["serial"],
         "step_us_p10_p50_p90": fig["step_us_p10_p50_p90"],
         "finalize_call_us": finalize_us,
-        "attention_two_stream": fig["attention"]["two_stream"],
+        "attention_call": fig["attention"]["call"],
         "serial_step": {"ms_per_step": tm["wall_serial"] * 1e3 / args.steps,
                         "tokens_per_s": wl.T * args.steps / tm["wall_serial"],
                         "step": "the same phases one after another on one stream, with HIP "

@@ -78,10 +78,12 @@ enum { RBKV_DTYPE_F32 = 0, RBKV_DTYPE_BF16 = 1 };
 
 /* Phases of ragged_blocked_attention (see ragged_blocked_attention_phase). */
 enum {
-  RBKV_PHASE_ALL = 0,     /* everything below, in this order */
+  RBKV_PHASE_ALL = 0,     /* ATTEND, then COMBINE */
   RBKV_PHASE_PREFILL = 1, /* multi-token chunks (bf16: matrix cores) */
   RBKV_PHASE_DECODE = 2,  /* single-token decodes, split-K (and float32 chunks) */
-  RBKV_PHASE_COMBINE = 3  /* log-sum-exp merge of the split-K partials */
+  RBKV_PHASE_COMBINE = 3, /* log-sum-exp merge of the split-K partials */
+  RBKV_PHASE_ATTEND = 4   /* PREFILL and DECODE work items together (one launch for the
+                             mixed batches of ragged_blocked_attention) */
 };
 
 /* Static shape of one attention layer and its KV pool, plus the batch capacities.
@@ -153,12 +155,12 @@ rbkv_status rbkv_metadata_bytes(const rbkv_shape* shape, size_t* dev_bytes,
 
 /* Device workspace ragged_blocked_attention needs for `batch` (split-K partial
  * results; the scratch output the blocked attention kernel is handed in the same
- * section), plus a 256-byte-aligned item counter for decodes that run as persistent
- * workgroups: bf16 batches over blocks of 64+ keys, groups of at most eight heads, with
- * both prefill chunks and decodes (ragged_blocked_attention_concurrent), and, at head
- * dim 128 with groups of 2-4 heads, any batch with decodes (the serial call as well).
- * The calls reset the counter themselves (a kernel, no memset).  0 when no decode is
- * split and no counter is needed.  Pure host computation. */
+ * section), plus a 256-byte-aligned block of item counters for work that runs as
+ * persistent workgroups: bf16 batches over blocks of 64+ keys with both prefill chunks
+ * and decodes, at head dim 64 with groups of at most eight heads, at head dim 128 with
+ * groups of up to 16; and, at head dim 128 with groups of 2-16 heads, any batch with
+ * decodes.  The calls reset the counters themselves (a kernel, no memset).  0 when no
+ * decode is split and no counter is needed.  Pure host computation. */
 rbkv_status rbkv_workspace_bytes(const rbkv_shape* shape, const rbkv_batch* batch,
                                  size_t* bytes);
 
@@ -216,7 +218,10 @@ rbkv_status blocked_kv_append_rotary(const rbkv_shape* shape, const rbkv_batch* 
  *   workspace device scratch of at least rbkv_workspace_bytes (may be NULL if 0)
  * Single-token decodes run as split-K streaming over 64-key tiles followed by a
  * log-sum-exp combine; bf16 prefill chunks run on MFMA tiles; float32 runs on the
- * vector ALUs throughout.  Accumulation is float32.
+ * vector ALUs throughout.  Accumulation is float32.  Batches with both chunks and
+ * decodes in bf16 at head dim 128, groups of 2-16 heads and blocks of 64+ keys run both
+ * kinds of work item in one launch of persistent workgroups (one per CU, each taking
+ * chunk tiles and decode items from counters in the workspace), then the combine.
  * Errors: INVALID_ARG, WORKSPACE, DEVICE_PTR, HIP. */
 rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* batch,
                                      const void* qkv, const void* kv_pool, void* out,
@@ -249,9 +254,13 @@ rbkv_status ragged_blocked_attention_noalloc(const rbkv_shape* shape, const rbkv
                                              void* stream);
 
 /* One phase of ragged_blocked_attention (RBKV_PHASE_*), for callers that place other
- * work between the phases or time them separately.  Running PREFILL, DECODE, COMBINE in
- * this order on one stream is exactly ragged_blocked_attention; COMBINE reads what
- * DECODE wrote to the workspace.  A phase with no work items returns OK without
+ * work between the phases or time them separately.  Running ATTEND then COMBINE on one
+ * stream is exactly ragged_blocked_attention (bit for bit).  PREFILL, DECODE, COMBINE in
+ * this order compute the same attention with the chunks and the decodes in separate
+ * launches; for the batches ragged_blocked_attention runs in one launch, the decodes then
+ * split their keys over four instead of eight wavefronts, so results agree to rounding
+ * (within the float32 accumulation), not bit for bit.  COMBINE reads what DECODE (or
+ * ATTEND) wrote to the workspace.  A phase with no work items returns OK without
  * launching.  Errors: as ragged_blocked_attention, plus INVALID_ARG for an unknown
  * phase. */
 rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_batch* batch,
@@ -259,20 +268,21 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
                                            void* out, void* workspace, size_t workspace_bytes,
                                            void* stream);
 
-/* ragged_blocked_attention with its two independent phases running at once: the
- * matrix-core prefill chunks on `stream`, the single-token decodes beside them on
- * `side_stream`, then the split-K combine on `stream` once both are done.  The phases
- * read the same inputs and write disjoint output rows, and every decode work item is
- * computed by one workgroup in the same order as in the serial call, so the result is
- * identical (bit for bit) to ragged_blocked_attention.  For bf16 groups of at most four
- * heads over blocks of 64+ keys the decodes run as persistent workgroups taking items
- * from a counter in the workspace (reset by the call): two per CU start beside the
- * prefill, and more join on `stream` once the prefill is done (two per CU with two LDS
- * tile stages each at head dim 128 and groups of 2-4 heads, else four), so the chip
- * is shared between the phases rather than split by kernel boundaries (about 10% less
- * time than the serial call on the full-budget and SplitFuse batches).  Other shapes
- * gain only where one phase leaves CUs idle.  Calls sharing a workspace must be ordered
- * (one stream).  The
+/* ragged_blocked_attention with its two independent phases running at once.  Batches
+ * that ragged_blocked_attention already runs in one launch (bf16, head dim 128, groups of
+ * 2-16 heads, blocks of 64+ keys) run exactly that on `stream` and leave the side
+ * stream and the events unused.  Otherwise the matrix-core prefill chunks run on
+ * `stream`, the single-token decodes beside them on `side_stream`, then the split-K
+ * combine on `stream` once both are done.  The phases read the same inputs and write
+ * disjoint output rows, and every decode work item is computed by one workgroup in the
+ * same order as in the serial call, so the result is identical (bit for bit) to
+ * ragged_blocked_attention.  For bf16 over blocks of 64+ keys (head dim 64 with groups of
+ * up to eight heads, head dim 128 with single-head groups) the decodes run as persistent
+ * workgroups taking items from a counter in the workspace (reset by the call): two per CU
+ * start beside the prefill, and more join on `stream` once the prefill is done, so the
+ * chip is shared between the phases rather than split by kernel boundaries.  Other
+ * shapes gain only where one phase leaves CUs idle.  Calls sharing a workspace must be
+ * ordered (one stream).  The
  * fork and join use two caller-owned events (hipEvent_t as void*, created by the
  * caller, e.g. with hipEventDisableTiming): fork_event is recorded on `stream` and
  * waited on by `side_stream`; join_event is recorded on `side_stream` and waited on by

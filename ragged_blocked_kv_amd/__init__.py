@@ -23,7 +23,7 @@ __all__ = [
     "ragged_blocked_attention_phase", "ragged_blocked_attention_concurrent",
     "ragged_embedding_gather", "ragged_logits_gather",
     "rbkv_kv_host_bytes", "blocked_kv_offload", "blocked_kv_restore", "EXPORTED_SYMBOLS", "PHASE_ALL", "PHASE_PREFILL",
-    "PHASE_DECODE", "PHASE_COMBINE",
+    "PHASE_DECODE", "PHASE_COMBINE", "PHASE_ATTEND",
     "OK", "ERR_INVALID_ARG", "ERR_CAPACITY", "ERR_BLOCKS", "ERR_UNSUPPORTED",
     "ERR_WORKSPACE", "ERR_DEVICE_PTR", "ERR_HIP", "ERR_HOST_MEMORY", "DTYPE_F32", "DTYPE_BF16",
 ]
@@ -31,7 +31,7 @@ __all__ = [
 OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_BLOCKS, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 ERR_WORKSPACE, ERR_DEVICE_PTR, ERR_HIP, ERR_HOST_MEMORY = 5, 6, 7, 8
 DTYPE_F32, DTYPE_BF16 = 0, 1
-PHASE_ALL, PHASE_PREFILL, PHASE_DECODE, PHASE_COMBINE = 0, 1, 2, 3
+PHASE_ALL, PHASE_PREFILL, PHASE_DECODE, PHASE_COMBINE, PHASE_ATTEND = 0, 1, 2, 3, 4
 STATIC_SCRATCH_BYTES = 64 << 20  # RBKV_STATIC_SCRATCH_BYTES
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librbkv.so")

@@ -445,11 +445,10 @@ rbkv_status ragged_blocked_attention_phase(const rbkv_shape* shape, const rbkv_b
                                            int32_t phase, const void* qkv, const void* kv_pool,
                                            void* out, void* workspace, size_t workspace_bytes,
                                            void* stream) {
-  if (phase < RBKV_PHASE_ALL || phase > RBKV_PHASE_COMBINE) return RBKV_ERR_INVALID_ARG;
-  const bool pre = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_PREFILL) && batch &&
-                   batch->n_prefill_items > 0;
-  const bool dec = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_DECODE) && batch &&
-                   batch->n_decode_items > 0;
+  if (phase < RBKV_PHASE_ALL || phase > RBKV_PHASE_ATTEND) return RBKV_ERR_INVALID_ARG;
+  const bool both = phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_ATTEND;
+  const bool pre = (both || phase == RBKV_PHASE_PREFILL) && batch && batch->n_prefill_items > 0;
+  const bool dec = (both || phase == RBKV_PHASE_DECODE) && batch && batch->n_decode_items > 0;
   const bool comb = (phase == RBKV_PHASE_ALL || phase == RBKV_PHASE_COMBINE) && batch &&
                     batch->n_combine_items > 0;
   bool launch = false;

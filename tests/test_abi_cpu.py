@@ -299,3 +299,18 @@ def test_concurrent_attention_argument_errors():
     assert f(join=None) == R.ERR_INVALID_ARG
     assert f(side=0x10) == R.ERR_INVALID_ARG  # the same stream twice
     assert f(shape=shape(head_dim=96)) == R.ERR_UNSUPPORTED  # checked before any fork
+
+
+def test_attention_phase_values():
+    """Phases 0..4 (ALL, PREFILL, DECODE, COMBINE, ATTEND) are accepted; anything else is
+    INVALID_ARG before any other check.  An empty batch launches nothing in any phase."""
+    s = shape()
+    b = R.Batch()
+    b.shape = s
+    for bad in (-1, 5, 99):
+        assert R.ragged_blocked_attention_phase(s, b, bad, FAKE, FAKE, FAKE, None, 0) == \
+            R.ERR_INVALID_ARG
+    assert (R.PHASE_ALL, R.PHASE_PREFILL, R.PHASE_DECODE, R.PHASE_COMBINE, R.PHASE_ATTEND) == \
+        (0, 1, 2, 3, 4)
+    for ph in range(5):
+        assert R.ragged_blocked_attention_phase(s, b, ph, FAKE, FAKE, FAKE, None, 0) == R.OK

@@ -1,6 +1,10 @@
-"""ragged_blocked_attention_concurrent (decodes on a side stream beside the prefill
-chunks, joined before the combine) gives exactly the bytes of the serial call, on mixed
-batches of both dtypes and on the full-budget and SplitFuse batches, repeatedly."""
+"""ragged_blocked_attention_concurrent gives exactly the bytes of the serial call, on mixed
+batches of both dtypes and on the full-budget and SplitFuse batches, repeatedly: the
+batches the library runs as one mixed launch (bf16, head dim 128, groups of 2-16 heads,
+64-key blocks) run that launch in both calls; the others put the decodes on a side
+stream beside the prefill chunks, joined before the combine.  The phase calls: ATTEND
+then COMBINE gives the bytes of the serial call; PREFILL, DECODE, COMBINE as separate
+launches agree with it to rounding."""
 import numpy as np
 import pytest
 import torch
@@ -77,3 +81,48 @@ def test_concurrent_equals_serial(name):
     serial = _run(wl, False, reps=1)[0]
     for k, got in enumerate(_run(wl, True)):
         assert np.array_equal(got, serial), k
+
+
+@pytest.mark.parametrize("name", ["full8192_gqa4", "splitfuse768_gqa4", "mfma_g12_mixed",
+                                  "lean_g4_d64"])
+def test_phase_calls(name):
+    from ragged_blocked_kv_amd import PHASE_ATTEND, PHASE_COMBINE, PHASE_DECODE, PHASE_PREFILL
+    from ragged_blocked_kv_amd.runtime import Engine
+    print(f"phases {name}", flush=True)
+    if name == "mfma_g12_mixed":
+        wl = W.random_workload(43, dtype="bf16", n_q_heads=24, n_kv_heads=2, head_dim=128,
+                               block_size=128, n_seqs=20, max_new=300, max_seen=4000)
+    elif name == "lean_g4_d64":
+        wl = W.random_workload(44, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=64,
+                               block_size=64, n_seqs=20, max_new=200, max_seen=3000)
+    else:
+        wl = W.make_workload(name)
+    assert (wl.n_new > 1).any() and (wl.n_new == 1).any()
+    dev = torch.device("cuda:0")
+    eng = Engine.for_workload(wl, device=dev)
+    qkv = W.make_qkv(wl).to(dev)
+    pool = W.make_pool_history(wl, device=dev)
+    eng.finalize(wl.n_new, wl.seen, wl.block_lists)
+    eng.append_rotary(qkv, pool, wl.rope_base)
+
+    def run(phases):
+        out = torch.full((wl.T, wl.n_q_heads, wl.head_dim), float("nan"), dtype=qkv.dtype,
+                         device=dev)
+        for ph in phases:
+            if ph is None:
+                eng.attention(qkv, pool, out)
+            else:
+                eng.attention_phase(ph, qkv, pool, out)
+        torch.cuda.synchronize()
+        return out
+
+    ref = run([None])
+    attend = run([PHASE_ATTEND, PHASE_COMBINE])
+    split = run([PHASE_PREFILL, PHASE_DECODE, PHASE_COMBINE])
+    bits = lambda t: t.view(torch.int16).cpu().numpy()
+    assert np.array_equal(bits(attend), bits(ref))
+    assert torch.isfinite(split).all()
+    err = (split.float() - ref.float()).abs().max().item()
+    # separate launches split each decode's keys over four wavefronts instead of eight:
+    # the same float32 sums in another order, then one bf16 rounding
+    assert err <= 2e-2, err

@@ -1,8 +1,10 @@
 """The attention calls under HIP graph capture: one step (device metadata rebuild, then the
-serial or the two-stream attention) captured once and replayed several times, with the
+serial or the concurrent attention) captured once and replayed several times, with the
 program's own eager work and synchronisations between the replays; every replay must give
-the bytes of the eager call.  The two-stream call's fork and join events, its side stream
-and its counter reset kernel are all captured (the library records no memset)."""
+the bytes of the eager call.  The concurrent call's fork and join events, its side stream
+and its counter reset kernels are all captured (the library records no memset); the
+full-budget and the eight-head-group batches take the mixed launch, the head-dim-64 batch
+the two streams."""
 import numpy as np
 import pytest
 import torch
@@ -18,13 +20,16 @@ def _bytes(t):
 
 @pytest.mark.parametrize("name,concurrent", [
     ("full8192_gqa4", True), ("full8192_gqa4", False), ("random_bf16_g8", True),
-    ("random_f32", True)])
+    ("random_bf16_d64", True), ("random_f32", True)])
 def test_graph_replays_match_eager(name, concurrent):
     from ragged_blocked_kv_amd.runtime import Engine
     print(f"graph {name} concurrent={concurrent}", flush=True)
     if name == "random_bf16_g8":
         wl = W.random_workload(41, dtype="bf16", n_q_heads=16, n_kv_heads=2, head_dim=128,
                                block_size=64, n_seqs=30, max_new=200, max_seen=3000)
+    elif name == "random_bf16_d64":
+        wl = W.random_workload(45, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=64,
+                               block_size=64, n_seqs=24, max_new=200, max_seen=3000)
     elif name == "random_f32":
         wl = W.random_workload(42, dtype="f32", n_q_heads=4, n_kv_heads=2, head_dim=64,
                                block_size=16, n_seqs=8, max_new=40, max_seen=300)
