@@ -727,8 +727,10 @@ def figures(wl, tm):
            "call": None}
     if tm["call_ms"] is not None:
         att["call"] = attention(float(np.median(tm["call_ms"])), tm["call_ms"])
+    both = bool((wl.n_new > 1).any()) and bool((wl.n_new == 1).any())
     att["timed_call"] = ("serial" if att["call"] is None else
-                         "mixed launch" if mixed_launch(wl) else "two streams")
+                         "mixed launch" if mixed_launch(wl) else
+                         "two streams" if both else "one stream")
     att["hbm_frac"] = (att["call"] or att["serial"])["hbm_frac_attention"]
     mixed = None
     if tm.get("mixed_ms") is not None:
