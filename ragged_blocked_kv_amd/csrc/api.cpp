@@ -125,14 +125,16 @@ bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
 
 // Split size for single-token decodes: about the kernel's target number of items overall.
 int32_t choose_split_tiles(const rbkv_shape& s, int64_t decode_tiles_total) {
+  const bool small_group = s.n_q_heads / s.n_kv_heads <= 4;
   const int64_t target =
-      decode_persistent_ok(s) ? (s.n_q_heads / s.n_kv_heads <= 4 ? DECODE_TARGET_ITEMS_LEAN
-                                                                : DECODE_TARGET_ITEMS_LEAN2)
+      decode_mfma_ok(s)       ? (small_group ? DECODE_TARGET_ITEMS_MFMA : DECODE_TARGET_ITEMS_MFMA_WIDE)
+      : decode_persistent_ok(s) ? (small_group ? DECODE_TARGET_ITEMS_LEAN : DECODE_TARGET_ITEMS_LEAN2)
       : decode_grouped(s)     ? DECODE_TARGET_ITEMS_GROUPED
                               : DECODE_TARGET_ITEMS;
+  const int64_t cap = decode_mfma_ok(s) ? MAX_SPLIT_TILES_MFMA : MAX_SPLIT_TILES;
   int64_t st = cdiv64(decode_tiles_total, target);
   if (st < MIN_SPLIT_TILES) st = MIN_SPLIT_TILES;
-  if (st > MAX_SPLIT_TILES) st = MAX_SPLIT_TILES;
+  if (st > cap) st = cap;
   return (int32_t)st;
 }
 
