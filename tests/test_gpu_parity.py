@@ -217,6 +217,39 @@ def test_edge_capacity_limits_exact():
     run_full(wl)
 
 
+MIXED_CASES = [  # name, Hq, Hkv, bs, (n_new, seen) per sequence: batches of the mixed launch
+    # many chunks and one decode: the decode list runs dry at once, its workgroups move on
+    ("one_decode_many_chunks", 16, 4, 64,
+     [(300, 500), (257, 0), (64, 2000), (1, 3000), (129, 64), (400, 1000), (77, 7)]),
+    # one short chunk and many decodes at groups of 16 over 128-key blocks
+    ("one_chunk_many_decodes_g16", 32, 2, 128,
+     [(45, 900)] + [(1, 300 + 97 * i) for i in range(40)]),
+    # one chunk and one decode with two kv heads: fewer kv groups than XCDs, so most
+    # XCDs' chunk lists are empty from the start and their workgroups take other lists
+    ("tiny_two_groups", 8, 2, 64, [(70, 130), (1, 5000)]),
+]
+
+
+@pytest.mark.parametrize("case", [c[0] for c in MIXED_CASES])
+def test_mixed_launch_edges(case):
+    """Batches the library runs as one mixed launch of chunk tiles and decode items, at
+    the edges of its work sharing; serial and concurrent calls against the oracle."""
+    name, Hq, Hkv, bs, seqs = next(c for c in MIXED_CASES if c[0] == case)
+    wl = W.random_workload(71, dtype="bf16", n_q_heads=Hq, n_kv_heads=Hkv, head_dim=128,
+                           block_size=bs, n_seqs=len(seqs))
+    wl.n_new = np.array([a for a, _ in seqs], dtype=np.int32)
+    wl.seen = np.array([b for _, b in seqs], dtype=np.int32)
+    need = [W.blocks_needed(a + b, bs) for a, b in seqs]
+    wl.num_blocks = sum(need) + 3
+    perm = np.random.default_rng(72).permutation(wl.num_blocks).astype(np.int32)
+    at = np.cumsum([0] + need)
+    wl.block_lists = [perm[at[i]:at[i + 1]] for i in range(len(seqs))]
+    wl.max_tokens = max(wl.max_tokens, int(wl.n_new.sum()))
+    wl.max_seqs = max(wl.max_seqs, len(seqs))
+    _say(f"case mixed {name}")
+    run_full(wl, concurrent=True)
+
+
 def test_long_prefill_chunk_many_tiles():
     """One long chunk with a long history next to decodes: several query tiles and
     many key tiles, masked diagonal tiles, ragged tails."""
