@@ -647,18 +647,16 @@ rbkv_status ragged_blocked_attention(const rbkv_shape* shape, const rbkv_batch* 
 
 namespace {
 
-// The two-stream call for shapes with a persistent decode: decode workgroups, two per CU,
-// start beside the prefill on the side stream and take the CUs it leaves; once the
-// prefill is done a second launch on the main stream joins them: two per CU of the
-// matrix-core kernel (two tile stages per wave; full-budget batch 1085 -> 1059 us and
-// SplitFuse 367 -> 359 us against the lean kernels), or four one-stage lean workgroups
-// per CU at head dim 64.  Both take items from one counter, so they finish together
-// whatever the split of the work.  (Sizes measured with the lean kernels on the
-// full-budget and SplitFuse batches: one per CU beside the prefill, or more than three,
-// was slower; the second launch's size matters within 1-2%.)
+// The two-stream call for the persistent-decode shapes that do not take the mixed launch
+// (head dim 64 with groups of up to eight heads, single-head groups at head dim 128):
+// decode workgroups, two per CU, start beside the prefill on the side stream and take
+// the CUs it leaves; once the prefill is done a second launch on the main stream joins
+// them, four per CU.  Both take items from one counter, so they finish together whatever
+// the split of the work.  (Sizes measured on the full-budget and SplitFuse batches when
+// they ran this way: one per CU beside the prefill, or more than three, was slower; the
+// second launch's size matters within 1-2%.)
 constexpr int OVERLAP_SIDE_WG_PER_CU = 2;
 constexpr int OVERLAP_MAIN_WG_PER_CU = 4;
-constexpr int OVERLAP_MAIN_WG_PER_CU_2ST = 2;
 rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                  const void* kv_pool, void* out, char* ws, hipStream_t hs,
                                  hipStream_t hside, hipEvent_t fork, hipEvent_t join) {
@@ -669,9 +667,6 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
   }
   int32_t* claim = (int32_t*)(ws + claim_offset(s, b));
   float* partials = (float*)ws;
-  // The matrix-core decode runs two tile stages per wave (66 KB, two workgroups per CU)
-  // on both streams; the head-dim-64 lean decode one stage (four per CU on the main stream).
-  const bool two_stage = decode_mfma_ok(s);
   // The counter reset runs on the side stream ahead of the side decodes, so the prefill
   // starts on the main stream at once; the join event is recorded right after the reset
   // and the main stream waits for that record before its own decode launch (long done by
@@ -685,9 +680,7 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
                                      OVERLAP_SIDE_WG_PER_CU * n_cu, hside, 1) == hipSuccess &&
             hipStreamWaitEvent(hs, join, 0) == hipSuccess &&
             launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,
-                                     (two_stage ? OVERLAP_MAIN_WG_PER_CU_2ST
-                                                : OVERLAP_MAIN_WG_PER_CU) * n_cu,
-                                     hs, two_stage ? 2 : 1) == hipSuccess;
+                                     OVERLAP_MAIN_WG_PER_CU * n_cu, hs, 1) == hipSuccess;
   // Join whatever was launched, so the caller's stream never runs ahead of the side work.
   const bool joined = hipEventRecord(join, hside) == hipSuccess &&
                       hipStreamWaitEvent(hs, join, 0) == hipSuccess;

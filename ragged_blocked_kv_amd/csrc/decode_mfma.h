@@ -8,8 +8,8 @@
 // LDS slices (global_load_lds_dwordx4, ST stages, the next slices in flight while this one
 // is computed).  Per step and wave:
 //   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 over four 32-dim steps: rows are the wave's 16
-//                   keys, columns the group's query heads (columns past G repeat the last
-//                   head), K fragments from LDS, Q^T in registers for the whole item;
+//                   keys, columns the group's query heads (columns past G hold zeros), K
+//                   fragments from LDS, Q^T in registers for the whole item;
 //   online softmax  lane (g, j) holds the scores of keys 4g..4g+3 for head j, so the
 //                   running maximum of head j is lane-local once the four lane groups
 //                   agree; it moves only past a slack of 2^8 (a cross-lane max when a lane
@@ -165,7 +165,7 @@ __device__ __forceinline__ void run_item(
     const uint32_t p23 = pack_bf16x2(__builtin_amdgcn_exp2f(sc[2] - m), __builtin_amdgcn_exp2f(sc[3] - m));
     l = __builtin_amdgcn_fdot2_f32_bf16(pair(p01), pair(0x3f803f80u), l, false);
     l = __builtin_amdgcn_fdot2_f32_bf16(pair(p23), pair(0x3f803f80u), l, false);
-    const s16x4v pb = __builtin_bit_cast(s16x4v, u32x2{p01, p23});
+    const s16x4v pb = __builtin_bit_cast(s16x4v, j < G ? u32x2{p01, p23} : u32x2{0u, 0u});
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const s16x4v vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4v*)(kt + vfo[d]));
@@ -187,6 +187,10 @@ __device__ __forceinline__ void run_item(
     const uint16_t* qrow = qkv + ((size_t)token * (Hq + 2 * Hkv) + (size_t)kvh * G + min(j, G - 1)) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = ld16(qrow + (4 * s + g) * 8);
+    if (j >= G) {  // padding columns multiply zeros (less switching in the matrix cores)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qb[s] = u32x4{0u, 0u, 0u, 0u};
+    }
     asm volatile("" : : "v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
   }
   int st = 0;

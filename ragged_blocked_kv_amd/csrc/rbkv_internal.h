@@ -178,8 +178,7 @@ hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* q
 // The decode as persistent workgroups draining the decode list through a device counter
 // (decode_persistent_ok shapes only); the counter must be zero when the first of the
 // launches sharing it starts (launch_decode_claim_reset).  stages: tile stages per wave
-// of the matrix-core kernel (2 or 3; fewer asks for 2) and per workgroup of the lean
-// kernel at head dim 64 (1 or 2, groups of up to four heads).
+// of the matrix-core kernel (3, or 2 for anything less); the other kernels have one form.
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
                                     int32_t workgroups, hipStream_t stream, int stages);
