@@ -424,7 +424,7 @@ rbkv_status launch_attention(const rbkv_shape& s, const rbkv_batch& b, bool pre,
       int n_cu = 0;
       int32_t* claim = (int32_t*)((char*)workspace + claim_offset(s, b));
       err = cu_count(&n_cu);
-      if (err == hipSuccess) err = launch_decode_claim_reset(claim, hs);
+      if (err == hipSuccess) err = launch_claims_reset(claim, 1, hs);
       if (err == hipSuccess)
         err = launch_decode_persistent(s, b, qkv, kv_pool, out, (float*)workspace, claim,
                                        SERIAL_PERSISTENT_WG_PER_CU * n_cu, hs,
@@ -673,7 +673,7 @@ rbkv_status attention_overlapped(const rbkv_shape& s, const rbkv_batch& b, const
   // the time the prefill ends), then recorded again at the end for the final join.
   bool ok = hipEventRecord(fork, hs) == hipSuccess &&
             hipStreamWaitEvent(hside, fork, 0) == hipSuccess &&
-            launch_decode_claim_reset(claim, hside) == hipSuccess &&
+            launch_claims_reset(claim, 1, hside) == hipSuccess &&
             hipEventRecord(join, hside) == hipSuccess &&
             launch_prefill(s, b, qkv, kv_pool, out, hs) == hipSuccess &&
             launch_decode_persistent(s, b, qkv, kv_pool, out, partials, claim,

@@ -1241,10 +1241,8 @@ hipError_t launch_lean(const rbkv_shape& s, const rbkv_batch& b, const void* qkv
   return hipGetLastError();
 }
 
-__global__ void lean_claim_reset_kernel(int32_t* claim) {
-  __hip_atomic_store(claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// Zeroes the item counters of a call (a kernel rather than a memset, so that a captured
+// graph holds no memset node).
 __global__ void claims_reset_kernel(int32_t* claims, int n) {
   if ((int)threadIdx.x < n)
     __hip_atomic_store(claims + threadIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1326,10 +1324,6 @@ hipError_t launch_claims_reset(int32_t* claims, int n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream) {
-  hipLaunchKernelGGL(lean_claim_reset_kernel, dim3(1), dim3(1), 0, stream, claim);
-  return hipGetLastError();
-}
 
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,

@@ -177,12 +177,11 @@ hipError_t launch_decode(const rbkv_shape& s, const rbkv_batch& b, const void* q
 
 // The decode as persistent workgroups draining the decode list through a device counter
 // (decode_persistent_ok shapes only); the counter must be zero when the first of the
-// launches sharing it starts (launch_decode_claim_reset).  stages: tile stages per wave
+// launches sharing it starts (launch_claims_reset).  stages: tile stages per wave
 // of the matrix-core kernel (3, or 2 for anything less); the other kernels have one form.
 hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                                     const void* pool, void* out, float* ws, int32_t* claim,
                                     int32_t workgroups, hipStream_t stream, int stages);
-hipError_t launch_decode_claim_reset(int32_t* claim, hipStream_t stream);
 
 hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                           const void* pool, void* out, hipStream_t stream);
