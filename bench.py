@@ -113,7 +113,7 @@ def decode_kernel_name(wl):
     matrix-core kernel for groups of 2-16 heads and the register-only kernel for single
     heads; at head dim 64 a lean workgroup with one K/V tile (one wave per head for groups
     of up to 4 heads, two heads per wave for 5-8); other bf16 groups of 5+ heads the
-    two-stage grouped kernel; float32, and bf16 groups of up to 4 over smaller blocks, one
+    grouped kernel (two LDS tile stages); float32, and bf16 groups of up to 4 over smaller blocks, one
     wave per item."""
     g = wl.n_q_heads // wl.n_kv_heads
     if wl.dtype == "bf16" and wl.block_size >= 64 and wl.head_dim == 128:

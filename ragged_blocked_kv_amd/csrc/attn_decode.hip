@@ -946,9 +946,10 @@ void decode_lean2_kernel(
 // Register-only decode for bf16 caches at head dim 128 over blocks of at least 64 keys,
 // for groups of up to GP query heads (heads past G repeat the last one and write nothing);
 // launched for single-head groups (GP = 1), where the lean kernel's four waves would
-// compute one head four times: MHA decode 167 -> 155 us, while groups of four heads
-// measured equal to the lean kernel and groups of eight 21% slower (the per-lane score
-// reduction grows with the group).  No LDS tile and no per-tile barrier: the four wavefronts of a workgroup
+// compute one head four times: MHA decode 167 -> 155 us (the matrix-core kernel, one of
+// its 16 columns used, 165-169 us), while groups of four heads measured equal to the lean
+// kernel and groups of eight 21% slower (the per-lane score reduction grows with the
+// group).  No LDS tile and no per-tile barrier: the four wavefronts of a workgroup
 // each take 16 keys of every 64-key tile of the item, loading them straight into
 // registers with coalesced non-temporal 16-byte loads (a wave instruction covers four
 // whole key rows), the next tile's loads issued before the current tile is computed.

@@ -47,14 +47,17 @@ enum HeaderWord {
 
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Single-token decodes of bf16 groups of five or more query heads run on the
+// Single-token decodes of bf16 groups of five or more query heads that no kernel below
+// takes (head dim 64 over blocks of fewer than 64 keys, or groups of 9-16 heads at head dim
+// 64; groups of 5-16 over blocks of fewer than 64 keys at head dim 128) run on the
 // one-wave-per-head kernel (shared LDS tiles); everything else on one wave per item.
 inline bool decode_grouped(const rbkv_shape& s) {
   return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads > 4;
 }
 
 // Single-token decodes of bf16 groups of at most eight query heads over blocks of 64 or
-// more keys run on the lean kernel (one wave per head, one K/V tile per workgroup).
+// more keys: at head dim 64 the lean kernels (one K/V tile per workgroup), at head dim 128
+// the register-only kernel for single-head groups (larger groups: decode_mfma_ok below).
 inline bool decode_lean_ok(const rbkv_shape& s) {
   return s.dtype == RBKV_DTYPE_BF16 && s.n_q_heads / s.n_kv_heads <= 8 && s.block_size >= 64;
 }

@@ -41,11 +41,11 @@ def _run(wl, concurrent, reps=3):
                                   "mfma_g16_d128", "lean_g6_d64", "splitfuse768_gqa4",
                                   "full8192_gqa4"])
 def test_concurrent_equals_serial(name):
-    """Shapes with a persistent decode (bf16 over 64-key blocks: the matrix-core kernel at
-    head dim 128 for groups of 2-16 heads, the register-only kernel for single heads, the
-    lean kernels at head dim 64) take the overlapped path: persistent decode workgroups on
-    both streams drain one item counter; each item is still computed by one workgroup in
-    the same order, so the bytes match."""
+    """Mixed batches at head dim 128 with groups of 2-16 heads run the mixed launch in both
+    calls.  The other persistent-decode shapes (bf16 over 64-key blocks: the register-only
+    kernel for single heads at head dim 128, the lean kernels at head dim 64) take the
+    overlapped path: persistent decode workgroups on both streams drain one item counter;
+    each item is still computed by one workgroup in the same order, so the bytes match."""
     print(f"concurrent {name}", flush=True)
     if name == "random_bf16":
         wl = W.random_workload(31, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128,
