@@ -127,7 +127,8 @@ bool same_shape(const rbkv_shape& a, const rbkv_shape& b) {
 int32_t choose_split_tiles(const rbkv_shape& s, int64_t decode_tiles_total) {
   const bool small_group = s.n_q_heads / s.n_kv_heads <= 4;
   const int64_t target =
-      decode_mfma_ok(s)       ? (small_group ? DECODE_TARGET_ITEMS_MFMA : DECODE_TARGET_ITEMS_MFMA_WIDE)
+      decode_mfma_ok(s) || decode_reg_ok(s)
+          ? (small_group ? DECODE_TARGET_ITEMS_MFMA : DECODE_TARGET_ITEMS_MFMA_WIDE)
       : decode_persistent_ok(s) ? (small_group ? DECODE_TARGET_ITEMS_LEAN : DECODE_TARGET_ITEMS_LEAN2)
       : decode_grouped(s)     ? DECODE_TARGET_ITEMS_GROUPED
                               : DECODE_TARGET_ITEMS;

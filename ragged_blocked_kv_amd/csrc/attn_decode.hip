@@ -1299,7 +1299,7 @@ hipError_t launch_g(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
     // heads: one K/V tile per workgroup, one wave per head up to 4 heads, two for 5-8.
     if constexpr (D == 128) {
       if (decode_mfma_ok(s)) return launch_mfma<2>(s, b, qkv, pool, out, ws, stream);
-      if (decode_lean_ok(s)) return launch_reg<1>(s, b, qkv, pool, out, ws, stream);
+      if (decode_reg_ok(s)) return launch_reg<1>(s, b, qkv, pool, out, ws, stream);
     } else {
       if (decode_lean_ok(s))
         return G <= 4 ? launch_lean<D, 4>(s, b, qkv, pool, out, ws, stream)
@@ -1332,7 +1332,7 @@ hipError_t launch_decode_persistent(const rbkv_shape& s, const rbkv_batch& b, co
   if (decode_mfma_ok(s))
     return stages >= 3 ? launch_mfma<3>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
                        : launch_mfma<2>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
-  if (s.head_dim == 128) return launch_reg<1>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
+  if (decode_reg_ok(s)) return launch_reg<1>(s, b, qkv, pool, out, ws, stream, claim, workgroups);
   return s.n_q_heads / s.n_kv_heads <= 4
              ? launch_lean<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups)
              : launch_lean2<64, 4>(s, b, qkv, pool, out, ws, stream, claim, workgroups);

@@ -34,7 +34,8 @@ constexpr int MAX_SPLIT_TILES = 64;
 // with still fewer, longer items: groups of up to four heads ~1k items, larger groups
 // ~2k with splits of up to 256 tiles (measured: full-budget decode 601 -> 594 us and
 // mixed launch 958 -> 943 us from 3072 items; long decode 2181 -> 2082 us from 6144 items
-// capped at 64 tiles; SplitFuse mixed launch 353 -> 342 us).
+// capped at 64 tiles; SplitFuse mixed launch 353 -> 342 us).  The register-only kernel
+// (single-head groups) takes ~1k too (MHA decode 154 -> 153 us).
 constexpr int64_t DECODE_TARGET_ITEMS_MFMA = 1024;
 constexpr int64_t DECODE_TARGET_ITEMS_MFMA_WIDE = 2048;
 constexpr int MAX_SPLIT_TILES_MFMA = 256;
@@ -68,6 +69,13 @@ inline bool decode_mfma_ok(const rbkv_shape& s) {
   const int32_t G = s.n_q_heads / s.n_kv_heads;
   return s.dtype == RBKV_DTYPE_BF16 && s.head_dim == 128 && s.block_size >= 64 && G >= 2 &&
          G <= MAX_GROUP;
+}
+
+// Single-token decodes of bf16 single-head groups at head dim 128 over blocks of 64 or
+// more keys run on the register-only kernel.
+inline bool decode_reg_ok(const rbkv_shape& s) {
+  return s.dtype == RBKV_DTYPE_BF16 && s.head_dim == 128 && s.block_size >= 64 &&
+         s.n_q_heads == s.n_kv_heads;
 }
 
 // Shapes whose decodes can run as persistent workgroups draining the decode list through
