@@ -250,6 +250,36 @@ def test_mixed_launch_edges(case):
     run_full(wl, concurrent=True)
 
 
+def _mixed_random_workload(seed):
+    """A random batch with both chunks and decodes for the mixed launch (redrawn under a
+    derived seed until it has both)."""
+    for attempt in range(50):
+        rng = np.random.default_rng(900 + seed + 1000 * attempt)
+        G = int(rng.choice([2, 3, 4, 6, 8, 12, 16]))
+        Hkv = int(rng.choice([1, 2, 4])) if G <= 8 else int(rng.choice([1, 2]))
+        bs = int(rng.choice([64, 128]))
+        frac = float(rng.choice([0.1, 0.3, 0.5, 0.7, 0.9]))
+        wl = W.random_workload(900 + seed + 1000 * attempt, dtype="bf16", n_q_heads=G * Hkv,
+                               n_kv_heads=Hkv, head_dim=128, block_size=bs,
+                               n_seqs=int(rng.integers(4, 40)),
+                               max_new=int(rng.choice([40, 150, 400])),
+                               max_seen=int(rng.choice([200, 1500, 6000])), decode_frac=frac,
+                               max_tokens=20000)
+        if (wl.n_new > 1).any() and (wl.n_new == 1).any():
+            return wl, G, Hkv, bs
+    raise AssertionError("no mixed draw")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mixed_launch_random(seed):
+    """Random batches of the mixed launch (bf16, head dim 128, groups of 2-16 heads, 64- or
+    128-key blocks) with every balance of chunks and decodes, from nearly all decodes to
+    nearly all chunks; serial and concurrent calls against the oracle."""
+    wl, G, Hkv, bs = _mixed_random_workload(seed)
+    _say(f"case mixed random seed={seed} G={G} Hkv={Hkv} bs={bs} S={wl.S} T={wl.T}")
+    run_full(wl, concurrent=True)
+
+
 def test_long_prefill_chunk_many_tiles():
     """One long chunk with a long history next to decodes: several query tiles and
     many key tiles, masked diagonal tiles, ragged tails."""
