@@ -13,17 +13,21 @@
 // p = seen + offset in the chunk) on the tiles that reach the diagonal only.
 //
 // Scheduling: waves w and w + 4 share a SIMD.  The two groups (waves 0-3, 4-7) alternate
-// between a matrix-core block (S^T of tile k and P.V of tile k-1) and a VALU block (the
+// between a matrix-core block (P.V of tile k-1 and S^T of tile k) and a VALU block (the
 // softmax of tile k), one block apart, so each SIMD's matrix core is fed by one wave while
 // the other computes weights; the matrix-core block runs at raised issue priority.
 //
 // Data movement: K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
-// staging registers) through a four-stage ring, two tiles ahead of use, issued by one
-// group during its VALU block; block ids come through the scalar cache two tiles ahead of
-// that.  Each lane's source address is chosen so that the LDS image carries an XOR
-// swizzle: K fragments (16 consecutive rows, one 16-byte chunk each) and transposing V
-// reads are both free of bank conflicts.  Work items are mapped onto block indices so that
-// the query tiles of one (sequence, kv head) run on the same XCD and share its L2.
+// staging registers) through a four-stage ring, two tiles ahead of use; block ids come
+// through the scalar cache two tiles ahead of that.  In the prefill kernel four more
+// wavefronts (one per SIMD, waves 8-11) issue every tile load and do nothing else, so the
+// load issue (tens of cycles per instruction while the texture path is busy) stays off
+// the compute waves; in the mixed kernel, which keeps eight wavefronts, group 1 issues
+// them during its VALU block.  Each lane's source address is chosen so that the LDS image
+// carries an XOR swizzle: K fragments (16 consecutive rows, one 16-byte chunk each) and
+// transposing V reads are both free of bank conflicts.  Work items are mapped onto block
+// indices so that the query tiles of one (sequence, kv head) run on the same XCD and share
+// its L2.
 //
 // Dynamic SplitFuse chunks continuing a sequence with seen cached tokens:
 // "DeepSpeed-Inference and DeepSpeed-MII", sections 10.3 and 10.10; query-tile sizing per
@@ -40,6 +44,7 @@ namespace {
 
 constexpr int PF_WAVES = PF_ROWS / 32;
 constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int PF_LW_THREADS = PF_THREADS + 256;  // eight compute and four loader wavefronts
 constexpr int STAGES = 4;  // K/V tiles resident in LDS: one computed, up to three in flight
 constexpr int N_XCD = 8;
 
@@ -76,17 +81,14 @@ __device__ __forceinline__ float pair_max(float v) {
 }
 __device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
-__device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // One work item (kv group gidx = (sequence, kv head), query tile jq of the sequence's nqt)
 // by the whole workgroup, with Ks / Vs the STAGES-tile K and V rings in LDS.  Every thread
-// of the workgroup calls it; it ends with every wave past its last barrier.  The pointers
-// must be the calling kernel's own restrict parameters (the block ids are read through
-// the scalar cache).
-template <int D>
+// of the workgroup calls it; it ends with every wave past its last barrier.  LW: the
+// workgroup has PF_THREADS + 256 threads and waves 8-11 are the loaders; otherwise it has
+// PF_THREADS and group 1 loads.  Ks and Vs must be 256-byte aligned (the fragment
+// addresses are formed by XOR).  The pointers must be the calling kernel's own restrict
+// parameters (the block ids are read through the scalar cache).
+template <int D, bool LW>
 __device__ __forceinline__ void prefill_item(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, int32_t qtt, const int32_t* __restrict__ cu,
@@ -96,7 +98,7 @@ __device__ __forceinline__ void prefill_item(
     int32_t seq, int32_t nqt, int32_t jq) {
   constexpr int CPR = D / 8;                   // 16-byte chunks per key row
   constexpr int TILE_CHUNKS = 64 * CPR;        // chunks per K (or V) tile
-  constexpr int LOADERS = PF_THREADS / 2;      // threads of the loading group
+  constexpr int LOADERS = PF_THREADS / 2;      // threads of the loading group (or waves)
   constexpr int NLD = TILE_CHUNKS / LOADERS;   // direct loads per loader per K (or V) tile
   constexpr int LPT = 2 * NLD;                 // vector-memory operations per loader per tile
   constexpr int ROWS_PER_LD = LOADERS / CPR;   // key rows between a loader's loads (16 or 32)
@@ -137,7 +139,7 @@ __device__ __forceinline__ void prefill_item(
   const int32_t rtok = rr / G, rhead = kvh * G + rr % G;
   const int32_t rpos = seen + q0 + rtok;
 
-  // Loader role (group 1).  Direct load i of loader lt fills LDS chunk i*LOADERS + lt of a
+  // Loader role (waves 8-11, or group 1).  Direct load i of loader lt fills LDS chunk i*LOADERS + lt of a
   // tile: key row i*ROWS_PER_LD + lt/CPR and, after the swizzle, one of its chunks.  The
   // swizzles depend on the row's low four bits only, so they are the same for every i.
   const int lt = tid & (LOADERS - 1);
@@ -196,6 +198,37 @@ __device__ __forceinline__ void prefill_item(
     }
   };
 
+  // Loader waves: the tile loads and waits that group 1 makes in the eight-wave form
+  // (described with the block sequence below), at the same barriers, and nothing else.
+  if constexpr (LW) {
+    if (wave >= PF_WAVES) {
+      int32_t ids[MAXNB];
+      fetch_ids(0, ids);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (j < ntile) issue_loads(j, ids, j);
+        fetch_ids(j + 1, ids);
+      }
+      if (ntile > 2) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      for (int32_t p = 0; p <= 2 * ntile; ++p) {  // phase p ends at the next barrier
+        if (p & 1) {
+          const int32_t k = p >> 1;
+          if (k + 2 < ntile) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+        } else if (p >= 2) {
+          const int32_t k = (p >> 1) - 1;
+          if (k + 3 < ntile) {
+            issue_loads(k + 3, ids, (k + 3) % STAGES);
+            fetch_ids(k + 4, ids);
+          }
+        }
+        __syncthreads();
+      }
+      return;
+    }
+  }
   u32x4 qb[KSTEPS];  // Q^T operand: k-step s holds dims 16s + 8*hl .. +8 of this lane's row
   f32x16 oacc[DB];
 #pragma unroll
@@ -213,79 +246,79 @@ __device__ __forceinline__ void prefill_item(
   const int vdim_in = 16 * (tg & 1) + 4 * trr;             // + 32d
   // K fragment of k-step s for key row col (row 32 + col sits 32 rows further: the
   // swizzle depends on the row's low bits only): element offset in a K tile.
-  int koff[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) koff[s] = (col * CPR + ((2 * s + hl) ^ kswz<CPR>(col))) * 8;
 
   // The two transposing reads that form the V^T fragment of step (kb, s2), dim block d.
-  auto vfrag = [&](const uint16_t* vt, int step, int d) {
-    const int kbase = 16 * step;  // step = 2 kb + s2: keys 32kb + 16s2
-    const int r0 = kbase + vkey_in, r1 = r0 + 8;
-    const int dim = 32 * d + vdim_in;
-    const int u = dim >> 3, half = dim & 7;
-    const u32x2 lo = ds_read_tr(vt + (r0 * CPR + (u ^ vswz<CPR>(r0))) * 8 + half);
-    const u32x2 hi = ds_read_tr(vt + (r1 * CPR + (u ^ vswz<CPR>(r1))) * 8 + half);
-    return u32x4{lo.x, lo.y, hi.x, hi.y};
+  // Byte offsets, within a stage of the K (V) ring, of this lane's first K fragment read
+  // (k-step 0, keys 0-31) and first V^T read (step 0, dim block 0).  With the swizzles
+  // above, k-step s sits at kA ^ (s << 5) (+ 32 rows for keys 32-63) and V^T step st,
+  // dim block d at (vB ^ (d << 6)) + 16 st rows (+ 8 rows for the second read): one XOR
+  // per fragment from a stage base that is a multiple of 256 bytes.
+  constexpr uint32_t RB = CPR * 16;  // bytes per key row
+  const uint32_t kA = [&] {
+    const int x = kswz<CPR>(col);
+    return (uint32_t)(col * RB + 32 * (x >> 1) + 16 * (hl ^ (x & 1)));
+  }();
+  const uint32_t vB = [&] {
+    const int r0 = vkey_in, u = vdim_in >> 3;
+    return (uint32_t)(2 * ((r0 * CPR + (u ^ vswz<CPR>(r0))) * 8 + (vdim_in & 7)));
+  }();
+  auto vfrag = [&](uint32_t vbase, int step, int d) {
+    const uint32_t a = (vbase ^ (uint32_t)(d << 6)) + step * 16 * RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(a + 8 * RB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
   };
-  // Matrix-core block: S^T of tile t (two 32-key blocks, k-step chains alternating), then
-  // O^T += V^T P^T of tile t-1.  For P.V, MFMA k index 8*hl + j of step (kb, s2) is key
+  // Matrix-core block: O^T += V^T P^T of tile t-1, then S^T of tile t (two 32-key blocks,
+  // k-step chains alternating).  For P.V, MFMA k index 8*hl + j of step (kb, s2) is key
   // 32kb + 16s2 + 8(j/4) + 4hl + j%4: exactly the keys this lane's P registers hold.
-  // LDS reads run a fixed distance ahead of the MFMAs that use them (K: two k-steps,
-  // V: one fragment per MFMA); scheduling fences keep the compiler from hoisting them
-  // further, which would only cost registers.
+  // P.V comes first so that the weights are dead before the scores are written: with the
+  // fragment addresses formed by XOR the kernel fits 168 registers (three wavefronts per
+  // SIMD) without spilling.  LDS reads run a fixed distance ahead of the MFMAs that use
+  // them (one V^T fragment, one K k-step); scheduling fences keep the compiler from
+  // hoisting them further, which would only cost registers.
   auto mblock = [&](int32_t t, auto do_qk, auto do_pv) {
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
-    // The SIMD's other wave runs its softmax meanwhile: issue priority goes to this
-    // block, so the matrix core is fed first and the VALU work fills the gaps.
     __builtin_amdgcn_s_setprio(1);
-    const uint16_t* kt = Ks[t % STAGES];
-    const uint16_t* vt = Vs[(t + STAGES - 1) % STAGES];
-    auto kfrag = [&](int s, int half) { return *(const u32x4*)(kt + koff[s] + half * 32 * D); };
-    u32x4 vc[DB];
-    if constexpr (QK) {
-      u32x4 k0[3], k1[3];  // ring of K fragments: k-steps s, s+1, s+2
-      k0[0] = kfrag(0, 0);
-      k1[0] = kfrag(0, 1);
-      k0[1] = kfrag(1, 0);
-      k1[1] = kfrag(1, 1);
+    const uint32_t kbase = lds_addr(Ks[t % STAGES]) + kA;
+    const uint32_t vt = lds_addr(Vs[(t + STAGES - 1) % STAGES]) + vB;
+    auto kfrag = [&](int s, int half) {
+      const uint32_t a = (kbase ^ (uint32_t)(s << 5)) + half * 32 * RB;
+      return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a;
+    };
+    constexpr int NV = 4 * DB;      // P.V MFMAs: step st = i / DB, dim block d = i % DB
+    constexpr int VA = 1;           // V fragments read ahead of their MFMA
+    u32x4 k0[2], k1[2];
+    if constexpr (PV) {
+      u32x4 vr[VA + 1];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        if (s + 2 < KSTEPS) {
-          k0[(s + 2) % 3] = kfrag(s + 2, 0);
-          k1[(s + 2) % 3] = kfrag(s + 2, 1);
-        } else if (PV) {
-          // The first P.V step's V fragments take the place of the K reads.
+      for (int i = 0; i < VA; ++i) vr[i] = vfrag(vt, i / DB, i % DB);
 #pragma unroll
-          for (int d = (s + 2 - KSTEPS) * DB / 2; d < (s + 3 - KSTEPS) * DB / 2; ++d)
-            vc[d] = vfrag(vt, 0, d);
-        }
+      for (int i = 0; i < NV; ++i) {
+        if (i + VA < NV) vr[(i + VA) % (VA + 1)] = vfrag(vt, (i + VA) / DB, (i + VA) % DB);
+        else if (QK && i + VA == NV) { k0[0] = kfrag(0, 0); k1[0] = kfrag(0, 1); }
         __builtin_amdgcn_sched_barrier(0);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(k0[s % 3]), as_bf16x8(qb[s]), s == 0 ? f32x16{} : sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(k1[s % 3]), as_bf16x8(qb[s]), s == 0 ? f32x16{} : sacc[1], 0, 0, 0);
+        oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(vr[i % (VA + 1)]), as_bf16x8(pb[i / DB]), oacc[i % DB], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-#pragma unroll
-      for (int d = 0; d < DB; ++d) vc[d] = vfrag(vt, 0, d);
+      k0[0] = kfrag(0, 0);
+      k1[0] = kfrag(0, 1);
     }
-    if constexpr (PV) {
+    if constexpr (QK) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        u32x4 vn[DB];
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          if (st + 1 < 4) vn[d] = vfrag(vt, st + 1, d);
-          __builtin_amdgcn_sched_barrier(0);
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vc[d]), as_bf16x8(pb[st]),
-                                                           oacc[d], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < KSTEPS; ++s) {
+        if (s + 1 < KSTEPS) {
+          k0[(s + 1) & 1] = kfrag(s + 1, 0);
+          k1[(s + 1) & 1] = kfrag(s + 1, 1);
         }
-        if (st + 1 < 4) {
-#pragma unroll
-          for (int d = 0; d < DB; ++d) vc[d] = vn[d];
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(k0[s & 1]), as_bf16x8(qb[s]), s == 0 ? f32x16{} : sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(k1[s & 1]), as_bf16x8(qb[s]), s == 0 ? f32x16{} : sacc[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -352,14 +385,14 @@ __device__ __forceinline__ void prefill_item(
   // feeds the matrix core while the other does the softmax.  In the barrier-delimited
   // phases p = 0 .. 2n+1, group 0 runs M_k in phase 2k and group 1 in phase 2k+1.
   //
-  // Tile loads, all by group 1: tiles 0, 1 and 2 in the prologue, tile k+3 at the start
-  // of its V_k (phase 2k+2) into the stage of tile k-1, whose last reader (group 1's
-  // M_k) ran in phase 2k+1.  After its M_k (phase 2k+1) group 1 waits for tile k+1,
-  // which group 0 reads first in phase 2k+2; tile k+2 (issued in phase 2k) may still be
-  // in flight.
+  // Tile loads, all by group 1 (by the loader waves when LW, in the same phases): tiles 0,
+  // 1 and 2 in the prologue, tile k+3 at the start of its V_k (phase 2k+2) into the stage
+  // of tile k-1, whose last reader (group 1's M_k) ran in phase 2k+1.  After its M_k
+  // (phase 2k+1) group 1 waits for tile k+1, which group 0 reads first in phase 2k+2;
+  // tile k+2 (issued in phase 2k) may still be in flight.
   int32_t ids[MAXNB];
-  fetch_ids(0, ids);
-  if (grp == 1) {
+  if (!LW) fetch_ids(0, ids);
+  if (!LW && grp == 1) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       if (j < ntile) issue_loads(j, ids, j);
@@ -374,7 +407,7 @@ __device__ __forceinline__ void prefill_item(
   // Tiles 0 and 1 and the Q^T operand resident; tile 2 may stay in flight.  Afterwards
   // no register load is outstanding: every vector-memory operation in the loop is a
   // tile load whose completion these waits track.
-  if (grp == 1 && ntile > 2) wait_vmcnt<LPT>();
+  if (!LW && grp == 1 && ntile > 2) wait_vmcnt<LPT>();
   else wait_vmcnt<0>();
   __syncthreads();
   if (grp == 1) __syncthreads();  // group 1 starts one phase behind
@@ -382,14 +415,14 @@ __device__ __forceinline__ void prefill_item(
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
   auto after_m = [&](int32_t kk) {  // group 1, end of M_kk: tile kk+1 resident
-    if (grp == 1) {
+    if (!LW && grp == 1) {
       if (kk + 2 < ntile) wait_vmcnt<LPT>();
       else wait_vmcnt<0>();
     }
     __syncthreads();
   };
   auto before_v = [&](int32_t kk) {  // group 1, start of V_kk: tile kk+3 into flight
-    if (grp == 1 && kk + 3 < ntile) {
+    if (!LW && grp == 1 && kk + 3 < ntile) {
       issue_loads(kk + 3, ids, (kk + 3) % STAGES);
       fetch_ids(kk + 4, ids);
     }
@@ -430,14 +463,14 @@ __device__ __forceinline__ void prefill_item(
 // XCDs, so each XCD gets an even share; the query tiles of one group run back to back on
 // one XCD (longest tile first) and share its L2.  Slots past a group's tiles exit.
 template <int D>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
+__global__ __launch_bounds__(PF_LW_THREADS, 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_groups, int32_t nq_max,
     int32_t qtt, const int32_t* __restrict__ cu, const int32_t* __restrict__ seen_arr,
     const int32_t* __restrict__ block_off, const int32_t* __restrict__ block_ids, int32_t Hq,
     int32_t Hkv, int32_t G, int32_t bs, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[STAGES][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[STAGES][64 * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[STAGES][64 * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[STAGES][64 * D];
   const int32_t xcd = (int32_t)(blockIdx.x % N_XCD);
   const int32_t k = (int32_t)(blockIdx.x / N_XCD);
   const int32_t gidx = (k / nq_max) * N_XCD + xcd;
@@ -446,8 +479,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_attn_kernel(
   const int32_t seq = rec.x, nqt = rec.y;
   const int32_t jq = k % nq_max;
   if (jq >= nqt) return;
-  prefill_item<D>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv, G, bs,
-                  scale_log2, Ks, Vs, gidx, seq, nqt, jq);
+  prefill_item<D, true>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv, G,
+                        bs, scale_log2, Ks, Vs, gidx, seq, nqt, jq);
 }
 
 // Mixed batches (bf16, head dim 128, groups of 2-16 heads, blocks of 64+ keys): one
@@ -472,7 +505,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
   constexpr int D = 128;
   constexpr int RING = STAGES * 64 * D;  // elements of the prefill's K (or V) ring
   static_assert(mfma_decode::buf_elems<2, PF_WAVES>() <= 2 * RING, "decode stages fit the ring");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * RING];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * RING];
   __shared__ float ml[mfma_decode::ml_floats<PF_WAVES>()];
   __shared__ int32_t claimed;
   uint16_t(*Ks)[64 * D] = (uint16_t(*)[64 * D])lds;
@@ -507,8 +540,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
       const int4 rec = pwork[gidx / Hkv];
       const int32_t jq = c % nq_max;
       if (jq >= rec.y) continue;
-      prefill_item<D>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv, G, bs,
-                      scale_log2, Ks, Vs, gidx, rec.x, rec.y, jq);
+      prefill_item<D, false>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv,
+                             G, bs, scale_log2, Ks, Vs, gidx, rec.x, rec.y, jq);
     }
   }
 }
@@ -520,7 +553,7 @@ hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, c
   const int32_t n_groups = b.n_prefill_seqs * s.n_kv_heads;
   const int32_t grid = ((n_groups + N_XCD - 1) / N_XCD) * b.prefill_qtiles_max * N_XCD;
   const int32_t qtt = q_tile_tokens(s.n_q_heads / s.n_kv_heads);
-  hipLaunchKernelGGL((prefill_attn_kernel<D>), dim3(grid), dim3(PF_THREADS), 0, stream,
+  hipLaunchKernelGGL((prefill_attn_kernel<D>), dim3(grid), dim3(PF_LW_THREADS), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out,
                      (const int4*)b.prefill_work, n_groups, b.prefill_qtiles_max, qtt,
                      b.cu_seqlens, b.seen, b.block_offsets,
