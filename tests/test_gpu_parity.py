@@ -296,6 +296,26 @@ def test_long_prefill_chunk_many_tiles():
     run_full(wl)
 
 
+@pytest.mark.parametrize("d,bs", [(128, 64), (128, 16), (64, 32)])
+def test_prefill_key_tile_counts(d, bs):
+    """Chunks only (the prefill launch alone): work items that see 1, 2, 3 and 4 key
+    tiles (64 keys each) and key counts one past and one short of a tile edge, so the
+    tile-load schedule's prologue and last steps run with every short count."""
+    seqs = [(64, 0), (2, 63), (64, 64), (65, 63), (3, 126), (64, 128), (10, 183), (200, 0),
+            (129, 255)]
+    wl = W.random_workload(11, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=d,
+                           block_size=bs, n_seqs=len(seqs))
+    wl.n_new = np.array([a for a, _ in seqs], dtype=np.int32)
+    wl.seen = np.array([b for _, b in seqs], dtype=np.int32)
+    need = [W.blocks_needed(a + b, bs) for a, b in seqs]
+    wl.num_blocks = sum(need) + 3
+    perm = np.random.default_rng(13).permutation(wl.num_blocks).astype(np.int32)
+    at = np.cumsum([0] + need)
+    wl.block_lists = [perm[at[i]:at[i + 1]] for i in range(len(seqs))]
+    _say(f"case prefill tile counts d={d} bs={bs}")
+    run_full(wl, concurrent=True)
+
+
 SPLIT_CASES = [  # name, dtype, Hq, Hkv, d, bs, (n_new, seen) per sequence
     # matrix-core kernel (G 4, d 128), one long decode beside a chunk
     ("mfma_g4_d128", "bf16", 8, 2, 128, 64, [(1, 20000), (40, 300), (1, 150), (1, 5000)]),
