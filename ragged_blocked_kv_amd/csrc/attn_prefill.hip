@@ -98,7 +98,7 @@ __device__ __forceinline__ void prefill_item(
     int32_t seq, int32_t nqt, int32_t jq) {
   constexpr int CPR = D / 8;                   // 16-byte chunks per key row
   constexpr int TILE_CHUNKS = 64 * CPR;        // chunks per K (or V) tile
-  constexpr int LOADERS = PF_THREADS / 2;      // threads of the loading group (or waves)
+  constexpr int LOADERS = PF_THREADS / 2;      // loader threads (group 1, or waves 8-11)
   constexpr int NLD = TILE_CHUNKS / LOADERS;   // direct loads per loader per K (or V) tile
   constexpr int LPT = 2 * NLD;                 // vector-memory operations per loader per tile
   constexpr int ROWS_PER_LD = LOADERS / CPR;   // key rows between a loader's loads (16 or 32)
@@ -139,7 +139,7 @@ __device__ __forceinline__ void prefill_item(
   const int32_t rtok = rr / G, rhead = kvh * G + rr % G;
   const int32_t rpos = seen + q0 + rtok;
 
-  // Loader role (waves 8-11, or group 1).  Direct load i of loader lt fills LDS chunk i*LOADERS + lt of a
+  // Loader role.  Direct load i of loader lt fills LDS chunk i*LOADERS + lt of a
   // tile: key row i*ROWS_PER_LD + lt/CPR and, after the swizzle, one of its chunks.  The
   // swizzles depend on the row's low four bits only, so they are the same for every i.
   const int lt = tid & (LOADERS - 1);
