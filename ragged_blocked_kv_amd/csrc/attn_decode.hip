@@ -1157,9 +1157,10 @@ void decode_reg_kernel(
 // Decode on the matrix cores (bf16, head dim 128, blocks of 64+ keys, groups of up to 16
 // heads): four wavefronts per workgroup, each streaming a 16-key slice of every 64-key
 // step through its own LDS stages (mfma_decode::run_item).  With a claim counter the
-// workgroups are persistent and take items from it.
+// workgroups are persistent and take items from it.  Two stages (66 KB of LDS) let two
+// workgroups share a CU, three (97 KB) one: the occupancy target follows.
 template <int ST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4 - ST, 4 - ST)))
 void decode_mfma_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ work,
