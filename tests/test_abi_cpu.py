@@ -109,6 +109,86 @@ def test_finalize_validation_errors():
     assert st == R.ERR_UNSUPPORTED
 
 
+def _expected_finalize_status(s, n_new, seen, lists):
+    """The validation rules of ragged_batch_finalize, in the order the header states them
+    (capacity, per-sequence counts, block coverage, block ids), for batches small enough
+    never to reach the work-list caps; None means valid."""
+    bs, nb = s.block_size, s.num_blocks
+    if len(n_new) > s.max_seqs:
+        return R.ERR_CAPACITY
+    T = nblk = 0
+    for n, sn, ids in zip(n_new, seen, lists):
+        if n < 1 or sn < 0:
+            return R.ERR_INVALID_ARG
+        T += n
+        if T > s.max_tokens:
+            return R.ERR_CAPACITY
+        B = -(-(sn + n) // bs)
+        if B > nb or len(ids) < B:
+            return R.ERR_BLOCKS
+        nblk += B
+        if nblk > nb:
+            return R.ERR_BLOCKS
+    used = set()
+    for n, sn, ids in zip(n_new, seen, lists):
+        for b in ids[: -(-(sn + n) // bs)]:
+            if b < 0 or b >= nb or b in used:
+                return R.ERR_BLOCKS
+            used.add(int(b))
+    return None
+
+
+def test_finalize_random_validation():
+    """Seeded random batches, each valid or carrying one kind of defect (too many
+    sequences or tokens, a zero or negative count, a short block list, an id out of range,
+    an id shared by two sequences): the status equals the rules above, and valid batches
+    get past validation to the first HIP call."""
+    import torch
+
+    rng = np.random.default_rng(2024)
+    s = shape(max_tokens=96, max_seqs=8, num_blocks=48, block_size=16)
+    kinds = ["valid", "seqs", "tokens", "count", "seen", "short", "range", "dup"]
+    seen_kinds = set()
+    for case in range(400):
+        kind = kinds[case % len(kinds)]
+        S = int(rng.integers(1, s.max_seqs + 1))
+        n_new = rng.integers(1, 12, size=S)
+        seen = rng.integers(0, 40, size=S)
+        if kind == "seqs":
+            S = s.max_seqs + 1
+            n_new, seen = np.ones(S, np.int64), np.zeros(S, np.int64)
+        elif kind == "tokens":
+            n_new[0] = s.max_tokens + 1 - (n_new.sum() - n_new[0])
+        elif kind == "count":
+            n_new[int(rng.integers(S))] = int(rng.integers(-3, 1))
+        elif kind == "seen":
+            seen[int(rng.integers(S))] = -int(rng.integers(1, 5))
+        need = [max(0, -(-(int(a) + int(b)) // s.block_size)) for a, b in zip(n_new, seen)]
+        ids = rng.permutation(s.num_blocks)
+        lists, at = [], 0
+        for b in need:
+            take = ids[at:at + b] if at + b <= s.num_blocks else np.arange(b)
+            lists.append(np.array(take, dtype=np.int32))
+            at += b
+        if kind == "short":
+            i = int(rng.integers(S))
+            lists[i] = lists[i][: max(0, len(lists[i]) - int(rng.integers(1, 3)))]
+        elif kind == "range":
+            i = int(rng.integers(S))
+            if len(lists[i]):
+                lists[i][int(rng.integers(len(lists[i])))] = rng.choice([-1, s.num_blocks, 10**6])
+        elif kind == "dup" and S > 1 and len(lists[0]) and len(lists[-1]):
+            lists[-1][-1] = lists[0][0]
+        want = _expected_finalize_status(s, n_new.tolist(), seen.tolist(), lists)
+        st, _ = finalize(s, n_new.astype(np.int32), seen.astype(np.int32), lists)
+        if want is None:
+            assert st in (R.ERR_DEVICE_PTR, R.ERR_HIP), (case, kind, st)
+        else:
+            assert st == want, (case, kind, st, want)
+        seen_kinds.add(kind if want is not None else "valid")
+    assert seen_kinds == set(kinds)
+
+
 def test_finalize_null_lists_and_negative_S():
     s = shape()
     d, h = sizes(s)
