@@ -31,12 +31,14 @@ constexpr int64_t DECODE_TARGET_ITEMS_LEAN2 = 6144;
 constexpr int MIN_SPLIT_TILES = 4;
 constexpr int MAX_SPLIT_TILES = 64;
 // The matrix-core decode (persistent workgroups, each wave streaming its own slices) wins
-// with still fewer, longer items: groups of up to four heads ~1k items, larger groups
+// with still fewer, longer items: groups of up to four heads ~512 items, larger groups
 // ~2k with splits of up to 256 tiles (measured: full-budget decode 601 -> 594 us and
-// mixed launch 958 -> 943 us from 3072 items; long decode 2181 -> 2082 us from 6144 items
-// capped at 64 tiles; SplitFuse mixed launch 353 -> 342 us).  The register-only kernel
-// (single-head groups) takes ~1k too (MHA decode 154 -> 153 us).
-constexpr int64_t DECODE_TARGET_ITEMS_MFMA = 1024;
+// mixed launch 958 -> 943 us from 3072 items to 1024; long decode 2181 -> 2082 us from
+// 6144 items capped at 64 tiles; SplitFuse mixed launch 353 -> 342 us with 1024 items,
+// 333 -> 329 us with 512, the full-budget batch equal at 512 and 256).  The register-only
+// kernel (single-head groups) takes the same target (MHA decode 154 -> 153 us at 1k; its
+// pairs are never long enough to split at 512).
+constexpr int64_t DECODE_TARGET_ITEMS_MFMA = 512;
 constexpr int64_t DECODE_TARGET_ITEMS_MFMA_WIDE = 2048;
 constexpr int MAX_SPLIT_TILES_MFMA = 256;
 
