@@ -1,5 +1,6 @@
-"""The benchmark's algorithmic work model (the numerator of every roofline figure)
-against a brute-force count over tokens, heads and visible keys on small batches."""
+"""The benchmark's arithmetic: its algorithmic work model (the numerator of every roofline
+figure) against a brute-force count over tokens, heads and visible keys on small batches,
+and the reduction of HBM counter runs to bytes per launch on synthetic counter files."""
 import os
 import sys
 
@@ -52,3 +53,47 @@ def test_algorithmic_work_full_budget_batch_figures():
     assert round(got["attention_bytes"] / 1e9, 3) == 4.522
     assert round(got["decode_bytes"] / 1e9, 3) == 4.114
     assert round(got["prefill_flops"] / 1e9, 1) == 520.5
+
+
+def _write_counter_csv(path, rows):
+    import csv
+
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for d, name, counter, value in rows:
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+def test_traffic_reduction_scales_by_the_copy_calibration(tmp_path):
+    """FETCH_SIZE / WRITE_SIZE (KiB, summed over a dispatch's rows) become bytes per launch
+    through the factor that makes a copy of known size read and write exactly its size;
+    the copy is the largest non-library dispatch, the kernel's launches are averaged."""
+    cal = 1 << 30
+    copy = "void at::native::copy_kernel(...)"
+    _write_counter_csv(tmp_path / "cf.csv", [(1, copy, "FETCH_SIZE", 12.0),
+                                            (2, copy, "FETCH_SIZE", 262144.0),  # two rows of one
+                                            (2, copy, "FETCH_SIZE", 262144.0)])  # dispatch: 512 MiB
+    _write_counter_csv(tmp_path / "cw.csv", [(2, copy, "WRITE_SIZE", 1048576.0)])
+    kern = "void rbkv::(anonymous namespace)::decode_mfma_kernel<3>(...)"
+    _write_counter_csv(tmp_path / "f.csv", [(7, kern, "FETCH_SIZE", 600.0), (7, kern, "FETCH_SIZE", 400.0),
+                                           (9, kern, "FETCH_SIZE", 1200.0),
+                                           (8, "void rbkv::combine_kernel<>(...)", "FETCH_SIZE", 5.0)])
+    _write_counter_csv(tmp_path / "w.csv", [(7, kern, "WRITE_SIZE", 10.0), (9, kern, "WRITE_SIZE", 30.0),
+                                           (8, "void rbkv::combine_kernel<>(...)", "WRITE_SIZE", 1.0)])
+    out = tmp_path / "traffic.json"
+    bench.traffic_from_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), cal,
+                                "toy", str(out))
+    import json
+
+    rec = json.load(open(out))
+    d = rec["attn_decode.hip:toy"]
+    assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
+    assert d["dispatches"] == 2
+    assert d["fetch_bytes_per_launch"] == 1100.0 * 1024 * 2.0   # mean of 1000 and 1200 KiB
+    assert d["write_bytes_per_launch"] == 20.0 * 1024           # mean of 10 and 30 KiB
+    assert d["bytes_per_launch"] == d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"]
+    assert rec["attn_combine.hip:toy"]["bytes_per_launch"] == 5.0 * 1024 * 2.0 + 1.0 * 1024
+    assert "attn_prefill.hip:toy" not in rec  # no dispatch of that group in the run
