@@ -97,3 +97,30 @@ def test_traffic_reduction_scales_by_the_copy_calibration(tmp_path):
     assert d["bytes_per_launch"] == d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"]
     assert rec["attn_combine.hip:toy"]["bytes_per_launch"] == 5.0 * 1024 * 2.0 + 1.0 * 1024
     assert "attn_prefill.hip:toy" not in rec  # no dispatch of that group in the run
+
+
+def test_mfma_reduction_per_launch_figures(tmp_path):
+    """Matrix-core counters of the prefill kernel become per-launch flops (512 per MOPS
+    unit), busy cycles, the busy fraction over the mean XCD's active cycles x 1024 SIMDs,
+    and rocprofv3's MfmaUtil averaged over the dispatches of its own run."""
+    kern = "void rbkv::(anonymous namespace)::prefill_attn_kernel<128>(...)"
+    other = "void rbkv::combine_kernel<>(...)"
+    rows = []
+    for d, busy, mops, gui in ((3, 600.0, 1000.0, 8000.0), (5, 500.0, 1000.0, 8000.0)):
+        rows += [(d, kern, "SQ_VALU_MFMA_BUSY_CYCLES", busy / 2), (d, kern, "SQ_VALU_MFMA_BUSY_CYCLES", busy / 2),
+                 (d, kern, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops), (d, kern, "GRBM_GUI_ACTIVE", gui),
+                 (d, kern, "SQ_BUSY_CU_CYCLES", 77.0)]
+    rows += [(4, other, "SQ_VALU_MFMA_BUSY_CYCLES", 9999.0), (4, other, "GRBM_GUI_ACTIVE", 1.0)]
+    _write_counter_csv(tmp_path / "m.csv", rows)
+    _write_counter_csv(tmp_path / "u.csv", [(3, kern, "MfmaUtil", 60.0), (5, kern, "MfmaUtil", 62.0)])
+    out = tmp_path / "mfma.json"
+    bench.mfma_from_counters(str(tmp_path / "m.csv"), str(tmp_path / "u.csv"), "toy", str(out))
+    import json
+
+    r = json.load(open(out))["attn_prefill.hip:toy"]
+    assert r["dispatches"] == 2
+    assert r["mfma_flops_per_launch"] == 1000.0 * 512
+    assert r["mfma_busy_cycles_per_launch"] == 550.0
+    assert r["gui_active_cycles_per_xcd"] == 1000.0
+    assert r["mfma_busy_frac_per_dispatch"] == [round(600.0 / (1000.0 * 1024), 4), round(500.0 / (1000.0 * 1024), 4)]
+    assert r["MfmaUtil_percent"] == 61.0
