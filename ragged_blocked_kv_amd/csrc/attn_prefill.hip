@@ -489,10 +489,10 @@ __global__ __launch_bounds__(PF_LW_THREADS, 1) void prefill_attn_kernel(
 // the first dec_first of its XCD (block b runs on XCD b % 8), on the prefill list
 // otherwise, and moves to the other list when its own is exhausted; it leaves when both
 // are.  Prefill items come from per-XCD lists (the placement of prefill_attn_kernel, with
-// a counter per XCD in claims[1 + xcd]; an XCD whose list is exhausted takes items from
-// the next ones), decode items from one list (claims[0]), eight wavefronts per item
-// (mfma_decode::run_item, two stages).  The ring of the prefill and the stages of the
-// decode share the LDS.  claims[0..8] must be zero at launch.
+// a counter per XCD in claims[1 + xcd]; a workgroup whose list is exhausted moves to the
+// list with the most slots left), decode items from one list (claims[0]), eight
+// wavefronts per item (mfma_decode::run_item, two stages).  The ring of the prefill and the
+// stages of the decode share the LDS.  claims[0..8] must be zero at launch.
 __global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, float* __restrict__ ws, const int4* __restrict__ pwork,
@@ -507,18 +507,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
   static_assert(mfma_decode::buf_elems<2, PF_WAVES>() <= 2 * RING, "decode stages fit the ring");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * RING];
   __shared__ float ml[mfma_decode::ml_floats<PF_WAVES>()];
-  __shared__ int32_t claimed;
+  __shared__ int32_t claimed, chosen;
   uint16_t(*Ks)[64 * D] = (uint16_t(*)[64 * D])lds;
   uint16_t(*Vs)[64 * D] = (uint16_t(*)[64 * D])(lds + RING);
   // XCD this workgroup runs on (hardware register XCC_ID, bits 0-3).
   const int32_t home = (int32_t)(__builtin_amdgcn_s_getreg(20 | (3 << 11)) & (N_XCD - 1));
   bool dec = (int32_t)(blockIdx.x / N_XCD) < dec_first;
   bool pre_left = n_groups > 0, dec_left = n_dec > 0;
-  int32_t xoff = 0;  // prefill list being drained: XCD home + xoff
+  int32_t xcd = home;  // prefill list being drained
+  const int32_t groups_per_list = (n_groups + N_XCD - 1) / N_XCD;
   while (pre_left || dec_left) {
     if (!pre_left) dec = true;
     if (!dec_left) dec = false;
-    const int32_t xcd = (home + xoff) & (N_XCD - 1);
     __syncthreads();  // the previous item is done with the LDS and the claim word
     if (threadIdx.x == 0) claimed = atomicAdd(dec ? &claims[0] : &claims[1 + xcd], 1);
     __syncthreads();
@@ -534,7 +534,27 @@ __global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
     } else {
       const int32_t gidx = (c / nq_max) * N_XCD + xcd;
       if (gidx >= n_groups) {
-        if (++xoff == N_XCD) pre_left = false;
+        // This list is exhausted: move to the one with the most slots left, or leave the
+        // prefill lists when none has any.  (Slots: list x holds the query tiles of
+        // groups x, x + 8, ...; its counter may run past them.)
+        if (threadIdx.x < 64) {
+          const int x = threadIdx.x & (N_XCD - 1);
+          const int32_t groups_x =
+              x < n_groups % N_XCD || n_groups % N_XCD == 0 ? groups_per_list : groups_per_list - 1;
+          const int32_t left =
+              threadIdx.x < N_XCD
+                  ? groups_x * nq_max -
+                        __hip_atomic_load(&claims[1 + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : -1;
+          int32_t best = left > 0 ? (left << 3) | x : -1;
+#pragma unroll
+          for (int o = 1; o < N_XCD; o <<= 1) best = max(best, __shfl_xor(best, o, 64));
+          if (threadIdx.x == 0) chosen = best < 0 ? -1 : (best & (N_XCD - 1));
+        }
+        __syncthreads();
+        const int32_t next = __builtin_amdgcn_readfirstlane(chosen);
+        if (next < 0) pre_left = false;
+        else xcd = next;
         continue;
       }
       const int4 rec = pwork[gidx / Hkv];
