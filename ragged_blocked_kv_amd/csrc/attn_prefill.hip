@@ -85,10 +85,12 @@ __device__ __forceinline__ float pair_sum(float v) { return v + __shfl_xor(v, 32
 // by the whole workgroup, with Ks / Vs the STAGES-tile K and V rings in LDS.  Every thread
 // of the workgroup calls it; it ends with every wave past its last barrier.  LW: the
 // workgroup has PF_THREADS + 256 threads and waves 8-11 are the loaders; otherwise it has
-// PF_THREADS and group 1 loads.  Ks and Vs must be 256-byte aligned (the fragment
-// addresses are formed by XOR).  The pointers must be the calling kernel's own restrict
-// parameters (the block ids are read through the scalar cache).
-template <int D, bool LW>
+// PF_THREADS and group 1 loads.  BIG: blocks of 64 keys or more (bs >= 64), so a 64-key
+// tile lies in one block (one block id per tile, one scalar base per load; the form for
+// smaller blocks stays out of the code).  Ks and Vs must be 256-byte aligned (the
+// fragment addresses are formed by XOR).  The pointers must be the calling kernel's own
+// restrict parameters (the block ids are read through the scalar cache).
+template <int D, bool LW, bool BIG>
 __device__ __forceinline__ void prefill_item(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, int32_t qtt, const int32_t* __restrict__ cu,
@@ -104,7 +106,7 @@ __device__ __forceinline__ void prefill_item(
   constexpr int ROWS_PER_LD = LOADERS / CPR;   // key rows between a loader's loads (16 or 32)
   constexpr int KSTEPS = D / 16;               // MFMA k-steps over the head dim
   constexpr int DB = D / 32;                   // 32-wide dim blocks of the output
-  constexpr int MAXNB = 4;                     // blocks a 64-key tile can span (block size 16)
+  constexpr int MAXNB = BIG ? 1 : 4;           // blocks a 64-key tile can span (1, or 4 at bs 16)
   static_assert(NLD >= 1 && ROWS_PER_LD % 16 == 0, "loader geometry");
   const int32_t kvh = gidx % Hkv;
   const int32_t qt = nqt - 1 - jq;
@@ -162,7 +164,7 @@ __device__ __forceinline__ void prefill_item(
   const uint32_t v_dst0 = __builtin_amdgcn_readfirstlane(lds_addr(&Vs[0][0]) + (wave & 3) * 64 * 16);
   auto issue_loads = [&](int32_t t, const int32_t* ids, int buf) {
     const uint32_t kd = k_dst0 + buf * TILE_BYTES, vd = v_dst0 + buf * TILE_BYTES;
-    if (bs >= 64) {
+    if constexpr (BIG) {
       // The tile sits in one block: a uniform base in scalar registers and 32-bit
       // per-thread offsets (measured 4% faster than 64-bit per-lane addresses).  Rows past
       // the end of a partial last tile load its last key (never read unmasked).
@@ -183,18 +185,18 @@ __device__ __forceinline__ void prefill_item(
           load_lds16_s(vbase, (uint32_t)(shift + v_src) * 2u, vd + i * LOADERS * 16);
         }
       }
-      return;
-    }
-    const int32_t b0 = (t * 64) >> bsh;
+    } else {
+      const int32_t b0 = (t * 64) >> bsh;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      // Rows past the end load the last key (never read unmasked).
-      const int32_t key = min(t * 64 + i * ROWS_PER_LD + lrow, n_keys - 1);
-      const int jb = (key >> bsh) - b0;
-      const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
-      const uint16_t* src = pool_g + (size_t)id * blk_stride + (size_t)(key & (bs - 1)) * D - lrow * D;
-      load_lds16(src + k_src, kd + i * LOADERS * 16);
-      load_lds16(src + v_off + v_src, vd + i * LOADERS * 16);
+      for (int i = 0; i < NLD; ++i) {
+        // Rows past the end load the last key (never read unmasked).
+        const int32_t key = min(t * 64 + i * ROWS_PER_LD + lrow, n_keys - 1);
+        const int jb = (key >> bsh) - b0;
+        const int32_t id = jb == 0 ? ids[0] : jb == 1 ? ids[1] : jb == 2 ? ids[2] : ids[3];
+        const uint16_t* src = pool_g + (size_t)id * blk_stride + (size_t)(key & (bs - 1)) * D - lrow * D;
+        load_lds16(src + k_src, kd + i * LOADERS * 16);
+        load_lds16(src + v_off + v_src, vd + i * LOADERS * 16);
+      }
     }
   };
 
@@ -462,7 +464,8 @@ __device__ __forceinline__ void prefill_item(
 // order of the ranked chunk sequences (longest first), are dealt round-robin over the
 // XCDs, so each XCD gets an even share; the query tiles of one group run back to back on
 // one XCD (longest tile first) and share its L2.  Slots past a group's tiles exit.
-template <int D>
+// BIG: blocks of 64 keys or more.
+template <int D, bool BIG>
 __global__ __launch_bounds__(PF_LW_THREADS, 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ pool,
     uint16_t* __restrict__ out, const int4* __restrict__ work, int32_t n_groups, int32_t nq_max,
@@ -479,8 +482,8 @@ __global__ __launch_bounds__(PF_LW_THREADS, 1) void prefill_attn_kernel(
   const int32_t seq = rec.x, nqt = rec.y;
   const int32_t jq = k % nq_max;
   if (jq >= nqt) return;
-  prefill_item<D, true>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv, G,
-                        bs, scale_log2, Ks, Vs, gidx, seq, nqt, jq);
+  prefill_item<D, true, BIG>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq,
+                             Hkv, G, bs, scale_log2, Ks, Vs, gidx, seq, nqt, jq);
 }
 
 // Mixed batches (bf16, head dim 128, groups of 2-16 heads, blocks of 64+ keys): one
@@ -560,20 +563,20 @@ __global__ __launch_bounds__(PF_THREADS, 1) void mixed_attn_kernel(
       const int4 rec = pwork[gidx / Hkv];
       const int32_t jq = c % nq_max;
       if (jq >= rec.y) continue;
-      prefill_item<D, false>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq, Hkv,
-                             G, bs, scale_log2, Ks, Vs, gidx, rec.x, rec.y, jq);
+      prefill_item<D, false, true>(qkv, pool, out, qtt, cu, seen_arr, block_off, block_ids, Hq,
+                                   Hkv, G, bs, scale_log2, Ks, Vs, gidx, rec.x, rec.y, jq);
     }
   }
 }
 
-template <int D>
+template <int D, bool BIG>
 hipError_t launch_t(const rbkv_shape& s, const rbkv_batch& b, const void* qkv, const void* pool,
                     void* out, hipStream_t stream) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int32_t n_groups = b.n_prefill_seqs * s.n_kv_heads;
   const int32_t grid = ((n_groups + N_XCD - 1) / N_XCD) * b.prefill_qtiles_max * N_XCD;
   const int32_t qtt = q_tile_tokens(s.n_q_heads / s.n_kv_heads);
-  hipLaunchKernelGGL((prefill_attn_kernel<D>), dim3(grid), dim3(PF_LW_THREADS), 0, stream,
+  hipLaunchKernelGGL((prefill_attn_kernel<D, BIG>), dim3(grid), dim3(PF_LW_THREADS), 0, stream,
                      (const uint16_t*)qkv, (const uint16_t*)pool, (uint16_t*)out,
                      (const int4*)b.prefill_work, n_groups, b.prefill_qtiles_max, qtt,
                      b.cu_seqlens, b.seen, b.block_offsets,
@@ -603,8 +606,12 @@ hipError_t launch_mixed(const rbkv_shape& s, const rbkv_batch& b, const void* qk
 hipError_t launch_prefill(const rbkv_shape& s, const rbkv_batch& b, const void* qkv,
                           const void* pool, void* out, hipStream_t stream) {
   if (s.dtype != RBKV_DTYPE_BF16) return hipErrorInvalidValue;  // float32 chunks use the VALU path
-  if (s.head_dim == 128) return launch_t<128>(s, b, qkv, pool, out, stream);
-  return launch_t<64>(s, b, qkv, pool, out, stream);
+  const bool big = s.block_size >= 64;
+  if (s.head_dim == 128)
+    return big ? launch_t<128, true>(s, b, qkv, pool, out, stream)
+               : launch_t<128, false>(s, b, qkv, pool, out, stream);
+  return big ? launch_t<64, true>(s, b, qkv, pool, out, stream)
+             : launch_t<64, false>(s, b, qkv, pool, out, stream);
 }
 
 }  // namespace rbkv
