@@ -296,11 +296,12 @@ def test_long_prefill_chunk_many_tiles():
     run_full(wl)
 
 
-@pytest.mark.parametrize("d,bs", [(128, 64), (128, 16), (64, 32)])
+@pytest.mark.parametrize("d,bs", [(128, 64), (128, 16), (64, 32), (128, 128), (64, 128)])
 def test_prefill_key_tile_counts(d, bs):
     """Chunks only (the prefill launch alone): work items that see 1, 2, 3 and 4 key
     tiles (64 keys each) and key counts one past and one short of a tile edge, so the
-    tile-load schedule's prologue and last steps run with every short count."""
+    tile-load schedule's prologue and last steps run with every short count; blocks of
+    16 and 32 keys (a tile spans several blocks), 64 and 128 (a tile lies in one block)."""
     seqs = [(64, 0), (2, 63), (64, 64), (65, 63), (3, 126), (64, 128), (10, 183), (200, 0),
             (129, 255)]
     wl = W.random_workload(11, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=d,
