@@ -124,3 +124,15 @@ def test_mfma_reduction_per_launch_figures(tmp_path):
     assert r["gui_active_cycles_per_xcd"] == 1000.0
     assert r["mfma_busy_frac_per_dispatch"] == [round(600.0 / (1000.0 * 1024), 4), round(500.0 / (1000.0 * 1024), 4)]
     assert r["MfmaUtil_percent"] == 61.0
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """The path runs on one GPU: bench.py --gpus N with N > 1 exits with status 2 and says
+    so on stderr, before it imports torch or touches a device."""
+    import subprocess
+    for n in (2, 8):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                           capture_output=True, text=True, timeout=120, cwd=ROOT)
+        assert r.returncode == 2, (n, r.returncode, r.stderr[-500:])
+        assert f"--gpus {n} is not supported" in r.stderr
+        assert r.stdout == ""
